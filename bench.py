@@ -1,0 +1,290 @@
+"""Benchmark of the window+sink chunk-attention hot path on one MI355X.
+
+One step = one pass of the layer workload (12 heads x 128, 1560 tokens/frame, chunk 3
+frames = 4680 query rows, sink 3 + window 9 frames, 20 chunks streamed from an empty cache):
+for each chunk, ll_attn_chunk then ll_cache_commit. Inputs are synthetic bf16 N(0, 0.25),
+generated on the GPU before timing (resident in HBM). Prints ONE JSON line.
+
+value = query rows attended per second over the whole step (attention + commit);
+roofline = the attention kernel against the bf16 dense MFMA peak, from HIP events recorded on
+the launch stream around every attention launch inside the timed region; extra rows report
+the commit, the FP4 path and the recache, each timed on its own after the main loop.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 (published)
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the FP4 / recache rows")
+    return ap.parse_args()
+
+
+def visible_keys(chunk, C, S, W, T):
+    s = chunk * C
+    frames = set(range(min(S, s + C))) | set(range(max(0, s - W), s)) | set(range(s, s + C))
+    return len(frames) * T
+
+
+def gen_inputs(torch, n_chunks, n, H, D, seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = []
+    for _ in range(n_chunks):
+        trip = []
+        for _ in range(3):
+            x = torch.randn((n, H, D), generator=g, device=device, dtype=torch.float32) * 0.5
+            trip.append(x.to(torch.bfloat16))
+        out.append(tuple(trip))
+    return out
+
+
+class EventTimer:
+    """Pairs of HIP events recorded on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s, tag):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((tag, s, e))
+
+    def totals(self):
+        out = {}
+        for tag, s, e in self.pairs:
+            ms = s.elapsed_time(e)
+            t = out.setdefault(tag, [0.0, 0])
+            t[0] += ms
+            t[1] += 1
+        return out
+
+
+def run_stream(cache, inputs, timer=None):
+    for c, (q, k, v) in enumerate(inputs):
+        if timer:
+            s = timer.start()
+        cache.attn_chunk(0, q, k, v, out=q.new_empty(q.shape) if False else _OUT[0])
+        if timer:
+            timer.stop(s, "attn")
+            s = timer.start()
+        cache.commit(0, k, v)
+        if timer:
+            timer.stop(s, "commit")
+
+
+_OUT = [None]
+
+
+def cpu_baseline(shape):
+    """The fp64 oracle on a bounded sample of the same workload: the steady-state chunk
+    (full window: 15 frames = 23400 keys) for 2 of the 12 heads and all 4680 rows, scaled
+    by flops to the whole 20-chunk stream."""
+    import numpy as np
+    from oracle.model import LayerModel
+    from windowed_attention_kv_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    Hs = 2
+    sub = synth.shrink(shape, heads=Hs)
+    m = LayerModel(sub.sink_frames, sub.window_frames, sub.chunk_frames, sub.tokens_per_frame,
+                   Hs, sub.head_dim)
+    steady = 5
+    for c in range(steady):
+        _, k, v = synth.chunk_inputs(sub, 0, 0, c)
+        m.commit(k.values, v.values)
+    q, k, v = synth.chunk_inputs(sub, 0, 0, steady)
+    t0 = time.perf_counter()
+    m.attn_chunk(q.values, k.values, v.values)
+    dt = time.perf_counter() - t0
+    n = shape.n_query
+    keys = visible_keys(steady, shape.chunk_frames, shape.sink_frames, shape.window_frames,
+                        shape.tokens_per_frame)
+    sample_flops = float(n) * keys * Hs * 4 * shape.head_dim
+    stream_flops = sum(float(n) * visible_keys(c, shape.chunk_frames, shape.sink_frames,
+                                               shape.window_frames, shape.tokens_per_frame)
+                       * shape.heads * 4 * shape.head_dim for c in range(shape.chunks))
+    stream_time = dt * stream_flops / sample_flops
+    return {"value": round(n * shape.chunks / stream_time, 3), "unit": "query-tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 oracle, steady chunk (23400 keys), {Hs}/12 heads x 4680 rows, "
+                       f"{dt:.2f} s measured, scaled by flops to the 20-chunk stream")}
+
+
+def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
+    """FP4 stream, standalone quant and the recache, each timed with events."""
+    res = {}
+    n, H, D = shape.n_query, shape.heads, shape.head_dim
+    inputs = gen_inputs(torch, shape.chunks, n, H, D, 7, "cuda")
+    out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+    # FP4 KV store at the layer shape
+    c4 = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
+               shape.window_frames, kv_format="fp4")
+    for rep in range(3):
+        c4.reset()
+        tm = EventTimer(torch)
+        for c, (q, k, v) in enumerate(inputs):
+            s = tm.start()
+            c4.attn_chunk(0, q, k, v, out=out)
+            tm.stop(s, "attn_steady" if c >= 4 else "attn_fill")
+            s = tm.start()
+            c4.commit(0, k, v)
+            tm.stop(s, "commit")
+        torch.cuda.synchronize()
+    tot = tm.totals()
+    steady_flops = attn_flops(n, 23400, H, D)
+    res["fp4_attention_steady"] = {
+        "ms": round(tot["attn_steady"][0] / tot["attn_steady"][1], 4),
+        "tflops": round(steady_flops / (tot["attn_steady"][0] / tot["attn_steady"][1]) / 1e9, 1)}
+    fp4_commit_bytes = n * H * D * 2 * 2 + 2 * n * H * (D // 2 + D // 16)
+    ms = tot["commit"][0] / tot["commit"][1]
+    res["fp4_commit"] = {"ms": round(ms, 5), "bytes": fp4_commit_bytes,
+                         "gbs": round(fp4_commit_bytes / ms / 1e6, 1)}
+    # standalone quant of one 12-frame cache (K and V): 2 x 18720 x 1536 elements
+    x = torch.randn((2 * 18720 * H, D), device="cuda").mul_(0.5).to(torch.bfloat16)
+    pk = torch.empty((x.shape[0], D // 2), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((x.shape[0], D // 16), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        kv_quant(x, pk, sc)
+    tm = EventTimer(torch)
+    for _ in range(10):
+        s = tm.start()
+        kv_quant(x, pk, sc)
+        tm.stop(s, "quant")
+    torch.cuda.synchronize()
+    ms = tm.totals()["quant"][0] / 10
+    qbytes = x.numel() * 2 + pk.numel() + sc.numel()
+    res["kv_quant_12_frames"] = {"ms": round(ms, 5), "bytes": qbytes,
+                                 "gbs": round(qbytes / ms / 1e6, 1)}
+    # recache of one layer at the prompt-switch shape (12 held frames, 512 text tokens)
+    cr = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
+               shape.window_frames)
+    for c in range(10):
+        cr.commit(0, inputs[c][1], inputs[c][2])
+    rows = 12 * shape.tokens_per_frame
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    big = [(torch.randn((rows, H, D), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+           for _ in range(4)]
+    txt = [(torch.randn((512, H, D), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+           for _ in range(2)]
+    o = torch.empty_like(big[0])
+    ox = torch.empty_like(big[0])
+    for _ in range(2):
+        cr.recache(0, big[0], big[1], big[2], big[3], txt[0], txt[1], out=o, out_x=ox)
+    tm = EventTimer(torch)
+    for _ in range(5):
+        s = tm.start()
+        cr.recache(0, big[0], big[1], big[2], big[3], txt[0], txt[1], out=o, out_x=ox)
+        tm.stop(s, "recache")
+    torch.cuda.synchronize()
+    ms = tm.totals()["recache"][0] / 5
+    # visible pairs: group g of 4680 rows sees (g+1)*4680 keys
+    self_pairs = sum(4680 * (g + 1) * 4680 for g in range(4))
+    fl = (self_pairs + rows * 512) * H * 4 * D
+    res["recache_layer"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                            "note": "self block-causal + cross (512 text keys) + rewrite, one layer"}
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path; the per-head sharding design is described in DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from windowed_attention_kv_amd import Cache, attn_flops, kv_quant, synth
+
+    shape = synth.CONFIGS["layer"]
+    n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
+    C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
+    torch.cuda.set_device(0)
+    inputs = gen_inputs(torch, shape.chunks, n, H, D, 1234, "cuda")
+    _OUT[0] = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+    cache = Cache(1, H, D, T, C, S, W)
+    flops_step = sum(attn_flops(n, visible_keys(c, C, S, W, T), H, D) for c in range(shape.chunks))
+
+    for _ in range(args.warmup):
+        cache.reset()
+        run_stream(cache, inputs)
+    torch.cuda.synchronize()
+
+    timer = EventTimer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        cache.reset()
+        run_stream(cache, inputs, timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tot = timer.totals()
+    ms_step = wall * 1e3 / args.steps
+    attn_ms = tot["attn"][0] / tot["attn"][1]            # average attention launch
+    attn_flops_launch = flops_step / shape.chunks          # average algorithmic flops per launch
+    achieved = attn_flops_launch / attn_ms / 1e9           # TFLOP/s
+    commit_ms = tot["commit"][0] / tot["commit"][1]
+    commit_bytes = 2 * 2 * n * H * D * 2                   # read + write of K and V
+
+    line = {
+        "metric": "query-tokens/s and TFLOP/s for window+sink chunk attention (% bf16 MFMA peak)",
+        "value": round(n * shape.chunks / (ms_step / 1e3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "layer: 12 heads x 128, 1560 tok/frame, chunk 3 (4680 q), sink 3, "
+                               "window 9, 20 chunks streamed (attn + commit per chunk)",
+                   "query_rows_per_step": n * shape.chunks,
+                   "attention_tflop_per_step": round(flops_step / 1e12, 4),
+                   "tflops_whole_step": round(flops_step / (ms_step / 1e3) / 1e12, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel<128,4,false>",
+                     "avg_launch_ms": round(attn_ms, 4),
+                     "avg_flops_per_launch": attn_flops_launch},
+        "rows": {"commit": {"avg_launch_ms": round(commit_ms, 5), "bytes": commit_bytes,
+                            "gbs": round(commit_bytes / commit_ms / 1e6, 1),
+                            "frac_hbm": round(commit_bytes / commit_ms / 1e6 / HBM_PEAK_GBS, 4)}},
+    }
+    if not args.no_extra:
+        line["rows"].update(extra_rows(torch, shape, Cache, kv_quant, attn_flops))
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(shape)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+"""CPU tests of the C-ABI boundary: the HIP library loads and exports every symbol that
+include/ll.h declares (no compute calls without a GPU), and the host layer's validation,
+error paths and launch arguments, run against a build of ll_host.cpp with a recording
+launch backend (libll_fake.so)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import ring
+from windowed_attention_kv_amd import _lib, make_desc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ll.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:ll_status|const char\*)\s+(ll_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared_functions() == sorted(_lib.SYMBOLS)
+
+
+def test_hip_library_exports_every_symbol():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libll.so not built")
+    l = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(l, name), name
+    assert "gfx950" in open(_lib.LIB_PATH, "rb").read().decode("latin-1"), "no gfx950 code object"
+
+
+@pytest.fixture
+def fake():
+    if not os.path.exists(_lib.FAKE_PATH):
+        pytest.skip("libll_fake.so not built")
+    f = _lib.load_fake()
+    f.llfake_reset()
+    return f
+
+
+def _create(f, **kw):
+    args = dict(layers=2, heads=2, head_dim=64, tokens_per_frame=16, chunk_frames=3,
+                sink_frames=3, window_frames=6, dtype="f32")
+    args.update(kw)
+    d = make_desc(**args)
+    size = ctypes.c_size_t()
+    assert f.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == 0
+    h = ctypes.c_void_p()
+    # the recording backend never touches this address
+    assert f.ll_cache_create(ctypes.byref(d), ctypes.c_void_p(1 << 20), size.value, ctypes.byref(h)) == 0
+    return h, size.value
+
+
+P = ctypes.c_void_p(1 << 24)  # aligned dummy device pointer
+
+
+def _records(f):
+    out = []
+    buf = (ctypes.c_int64 * 16)()
+    for i in range(f.llfake_count()):
+        kind = f.llfake_record(i, buf)
+        out.append((kind, list(buf)))
+    return out
+
+
+def _state(f, h, layer, slots):
+    F = ctypes.c_int64()
+    sl = (ctypes.c_int32 * slots)()
+    assert f.ll_cache_state(h, layer, ctypes.byref(F), sl) == 0
+    return F.value, list(sl)
+
+
+def _kernel_slot(rec, r):
+    """Destination slot of source frame rank r as the scatter kernel computes it (launch.h)."""
+    n_frames, n_lead, lead0, S, W, first_ring = rec[5], rec[6], rec[7], rec[8], rec[9], rec[10]
+    if r < n_lead:
+        return lead0 + r
+    return S + (first_ring + r - n_lead) % W
+
+
+@pytest.mark.parametrize("S,W,C", [(3, 6, 3), (3, 9, 3), (2, 5, 3), (0, 4, 2), (4, 3, 1), (5, 2, 3)])
+def test_commit_slots_and_state_follow_the_ring(fake, S, W, C):
+    h, _ = _create(fake, sink_frames=S, window_frames=W, chunk_frames=C)
+    for chunk in range(25):
+        F = chunk * C
+        fake.llfake_reset()
+        assert fake.ll_attn_chunk(h, 1, P, P, P, P, None) == 0
+        assert fake.ll_cache_commit(h, 1, P, P, None) == 0
+        (ka, att), (kc, com) = _records(fake)
+        assert ka == 0 and kc == 1
+        # attention reads exactly the held frames' slots (a prefix) plus the own chunk
+        assert att[4] == ring.valid_slots(F, S, W) * 16
+        assert att[8] == C * 16 and att[11] == 0
+        # the commit writes frame F+i into ring.slot_of_frame(F+i)
+        assert com[5] == C
+        for i in range(C):
+            assert _kernel_slot(com, i) == ring.slot_of_frame(F + i, S, W)
+        Fs, slots = _state(fake, h, 1, S + W)
+        assert Fs == F + C and slots == ring.slot_map(F + C, S, W)
+        # layer 0 untouched
+        assert _state(fake, h, 0, S + W) == (0, [-1] * (S + W))
+    fake.ll_cache_destroy(h)
+
+
+@pytest.mark.parametrize("chunks", [1, 2, 3, 4, 5, 9])
+def test_recache_launches(fake, chunks):
+    S, W, C, T = 3, 9, 3, 16
+    h, _ = _create(fake, sink_frames=S, window_frames=W, chunk_frames=C, dtype="bf16")
+    for _ in range(chunks):
+        assert fake.ll_cache_commit(h, 0, P, P, None) == 0
+    F = chunks * C
+    held = ring.held_frames(F, S, W)
+    fake.llfake_reset()
+    assert fake.ll_recache(h, 0, P, P, P, P, P, P, 512, P, P, None) == 0
+    recs = _records(fake)
+    assert [k for k, _ in recs] == [0, 0, 1]
+    self_att, cross, rewrite = recs[0][1], recs[1][1], recs[2][1]
+    assert self_att[3] == len(held) * T and self_att[4] == len(held) * T and self_att[11] == 1
+    assert self_att[12] == min(F, S) and self_att[13] == max(S, F - W) and self_att[14] == F
+    assert cross[3] == len(held) * T and cross[4] == 512 and cross[11] == 0
+    assert rewrite[5] == len(held)
+    for r, f in enumerate(held):
+        assert _kernel_slot(rewrite, r) == ring.slot_of_frame(f, S, W)
+    # the recache keeps frame ids and slots
+    assert _state(fake, h, 0, S + W) == (F, ring.slot_map(F, S, W))
+    fake.ll_cache_destroy(h)
+
+
+def _limit_closed_form(row, T, C, n_sink, base, F):
+    """The kernels' per-row key limit (launch.h Visibility mode 1)."""
+    r = row // T
+    f = r if r < n_sink else base + (r - n_sink)
+    X = (f // C + 1) * C
+    return T * (min(n_sink, X) + max(0, min(F, X) - base))
+
+
+@pytest.mark.parametrize("S,W,C,chunks", [(3, 9, 3, 10), (3, 9, 3, 2), (2, 5, 3, 7), (4, 6, 2, 9)])
+def test_recache_key_limit_matches_block_causal_mask(S, W, C, chunks):
+    from oracle.model import LayerModel
+    T = 4
+    F = chunks * C
+    m = LayerModel(S, W, C, T, 1, 16)
+    m.F = F
+    frames = m.held()
+    mask = m.recache_mask(frames)(range(len(frames) * T))
+    for row in range(len(frames) * T):
+        lim = _limit_closed_form(row, T, C, min(F, S), max(S, F - W), F)
+        assert list(mask[row]) == [j < lim for j in range(len(frames) * T)]
+
+
+def test_errors_leave_state_unchanged(fake):
+    h, size = _create(fake)
+    st = _state(fake, h, 0, 9)
+    assert fake.ll_attn_chunk(h, 2, P, P, P, P, None) == _lib.LL_EINVAL      # bad layer
+    assert fake.ll_attn_chunk(h, -1, P, P, P, P, None) == _lib.LL_EINVAL
+    assert fake.ll_cache_commit(h, 0, None, P, None) == _lib.LL_EINVAL       # null pointer
+    assert fake.ll_cache_commit(h, 0, ctypes.c_void_p((1 << 24) + 8), P, None) == _lib.LL_EINVAL
+    assert b"aligned" in fake.ll_last_error()
+    assert fake.ll_recache(h, 0, P, P, P, P, P, P, 16, P, P, None) == _lib.LL_ESTATE  # empty
+    assert fake.ll_cache_commit(h, 0, P, P, None) == 0
+    assert fake.ll_recache(h, 0, P, P, P, P, P, P, 0, P, P, None) == _lib.LL_EINVAL   # n_text
+    fake.llfake_fail_next(1)
+    assert fake.ll_cache_commit(h, 0, P, P, None) == _lib.LL_EDEVICE             # launch fails
+    assert b"injected" in fake.ll_last_error()
+    assert _state(fake, h, 0, 9)[0] == 3          # only the successful commit counted
+    assert fake.llfake_count() == 1
+    assert fake.ll_cache_commit(h, 0, P, P, None) == 0
+    assert fake.ll_last_error() == b""
+    assert _state(fake, h, 0, 9)[0] == 6
+    assert fake.ll_cache_reset(h) == 0
+    assert _state(fake, h, 0, 9) == st
+    fake.ll_cache_destroy(h)
+
+
+def test_descriptor_validation(fake):
+    size = ctypes.c_size_t()
+    bad = [dict(head_dim=96), dict(head_dim=0), dict(window_frames=0), dict(sink_frames=-1),
+           dict(tokens_per_frame=0), dict(chunk_frames=0), dict(layers=0), dict(heads=0)]
+    for kw in bad:
+        args = dict(layers=1, heads=2, head_dim=64, tokens_per_frame=16, chunk_frames=3,
+                    sink_frames=3, window_frames=6)
+        args.update(kw)
+        d = make_desc(**args)
+        assert fake.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) != 0, kw
+    d = make_desc(1, 2, 64, 16, 3, 3, 6, dtype="f32", kv_format="fp4")
+    assert fake.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == _lib.LL_EUNSUPPORTED
+    d = make_desc(1, 2, 64, 16, 3, 3, 6)
+    d.abi_version = 99
+    assert fake.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == _lib.LL_EINVAL
+    # too little or misaligned device memory
+    d = make_desc(1, 2, 64, 16, 3, 3, 6)
+    assert fake.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == 0
+    h = ctypes.c_void_p()
+    assert fake.ll_cache_create(ctypes.byref(d), P, size.value - 1, ctypes.byref(h)) == _lib.LL_EINVAL
+    assert fake.ll_cache_create(ctypes.byref(d), ctypes.c_void_p((1 << 24) + 16), size.value,
+                                ctypes.byref(h)) == _lib.LL_EINVAL
+
+
+def test_cache_bytes():
+    """Cache size depends only on S+W (and the shape), per layer: 12 frames of 1560 tokens x
+    12 heads x 128 in bf16, K and V = 115.0 MB; FP4: 4.5 bits per element."""
+    if not os.path.exists(_lib.FAKE_PATH):
+        pytest.skip("libll_fake.so not built")
+    f = _lib.load_fake()
+    size = ctypes.c_size_t()
+    d = make_desc(1, 12, 128, 1560, 3, 3, 9)
+    assert f.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == 0
+    assert size.value == 2 * 12 * 1560 * 12 * 128 * 2
+    d = make_desc(30, 12, 128, 1560, 3, 3, 9, kv_format="fp4")
+    assert f.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == 0
+    elems = 12 * 1560 * 12 * 128
+    assert size.value == 30 * 2 * (elems // 2 + elems // 16)
+
+
+def test_kv_quant_validation(fake):
+    assert fake.ll_kv_quant(P, 4, 24, P, P, None) == _lib.LL_EINVAL
+    assert fake.ll_kv_quant(P, -1, 16, P, P, None) == _lib.LL_EINVAL
+    assert fake.ll_kv_quant(P, 0, 16, P, P, None) == 0
+    assert fake.ll_kv_quant(P, 3, 32, None, P, None) == _lib.LL_EINVAL
+    fake.llfake_reset()
+    assert fake.ll_kv_quant(P, 3, 32, P, P, None) == 0
+    assert _records(fake)[0][0] == 2

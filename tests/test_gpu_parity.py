@@ -1,0 +1,258 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bit-exact: slot maps, exported cache bytes (dense copies, FP4 packed codes and scales),
+ll_kv_quant. Toleranced: attention outputs (bf16: max-abs <= 1e-2 and rel-L2 <= 5e-3; fp32:
+1e-5), compared per call against the unrounded oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from _parity import assert_close, log, sample_rows, to_np
+from oracle import fp4 as ofp4
+from oracle import ring
+from oracle.model import LayerModel
+from windowed_attention_kv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _cache(shape, kv_format="dense", layers=1):
+    from windowed_attention_kv_amd import Cache
+    return Cache(layers, shape.heads, shape.head_dim, shape.tokens_per_frame, shape.chunk_frames,
+                 shape.sink_frames, shape.window_frames, dtype=shape.dtype, kv_format=kv_format)
+
+
+def _model(shape, kv_format="dense"):
+    return LayerModel(shape.sink_frames, shape.window_frames, shape.chunk_frames,
+                      shape.tokens_per_frame, shape.heads, shape.head_dim, kv_format=kv_format)
+
+
+def _check_export(cache, model, shape, layer=0):
+    import torch
+    torch.cuda.synchronize()
+    F, slots = cache.state(layer)
+    assert F == model.F and slots == model.slot_map()
+    T, H = shape.tokens_per_frame, shape.heads
+    if cache.kv_format == "fp4":
+        kp, ks, vp, vs = (x.cpu().numpy() for x in cache.export(layer))
+        mkp, mks, mvp, mvs, valid = model.export_fp4()
+        for got, want, name in ((kp, mkp, "K packed"), (ks, mks, "K scales"),
+                                (vp, mvp, "V packed"), (vs, mvs, "V scales")):
+            np.testing.assert_array_equal(got[valid], want[valid], err_msg=name)
+    else:
+        K, V = (to_np(x) for x in cache.export(layer))
+        MK, MV = model.export_dense()
+        valid = ~np.isnan(MK[:, 0, 0])
+        np.testing.assert_array_equal(K[valid], MK[valid])
+        np.testing.assert_array_equal(V[valid], MV[valid])
+        assert valid.sum() == ring.valid_slots(model.F, shape.sink_frames, shape.window_frames) * T
+
+
+def run_stream(shape, n_chunks, kv_format="dense", compare=None, rows=None, steps=1,
+               export_every=True, **kw):
+    """Stream n_chunks through the library and the oracle; compare the chunks in `compare`
+    (default all) on `rows` (default all) for every denoise step."""
+    cache = _cache(shape, kv_format)
+    model = _model(shape, kv_format)
+    worst = (0.0, 0.0)
+    for c in range(n_chunks):
+        for step in range(steps):
+            q, k, v = synth.chunk_inputs(shape, 0, step, c, **kw)
+            tq, tk, tv = q.torch("cuda"), k.torch("cuda"), v.torch("cuda")
+            o = cache.attn_chunk(0, tq, tk, tv)
+            if compare is None or c in compare:
+                r = rows if rows is not None else np.arange(shape.n_query)
+                ref = model.attn_chunk(q.values, k.values, v.values, rows=r)
+                ma, rl = assert_close(to_np(o)[r], ref, shape.dtype, f"chunk {c} step {step}")
+                worst = (max(worst[0], ma), max(worst[1], rl))
+        cache.commit(0, tk, tv)
+        model.commit(k.values, v.values, k.bits, v.bits)
+        if export_every or c == n_chunks - 1:
+            _check_export(cache, model, shape)
+    log(f"{shape.name} {kv_format}: worst max-abs {worst[0]:.3e} rel-L2 {worst[1]:.3e}")
+    return cache, model
+
+
+def test_tiny_fp32_stream():
+    log("case: tiny fp32 stream, 8 chunks")
+    run_stream(synth.CONFIGS["tiny"], 8)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_bf16_ragged_stream(D):
+    shape = synth.shrink(synth.CONFIGS["layer"], name=f"ragged-d{D}", heads=3, head_dim=D,
+                         tokens_per_frame=100, window_frames=5)
+    log(f"case: bf16 ragged stream D={D}")
+    run_stream(shape, 9)
+
+
+def test_bf16_peaked_and_frame_offsets():
+    shape = synth.shrink(synth.CONFIGS["layer"], name="peaked", heads=2, tokens_per_frame=72,
+                         window_frames=4)
+    log("case: bf16 peaked Q/K, V with per-frame offsets")
+    run_stream(shape, 7, peaked=True, v_frame_offset=0.25)
+
+
+def test_denoise_steps_only_last_commits():
+    shape = synth.shrink(synth.CONFIGS["layer"], name="steps", heads=2, tokens_per_frame=40,
+                         window_frames=4)
+    log("case: 4 denoise steps per chunk")
+    run_stream(shape, 6, steps=4)
+
+
+def test_fp32_head_dim_128_and_sink_variants():
+    shape = synth.shrink(synth.CONFIGS["tiny"], name="f32-d128", head_dim=128, sink_frames=2,
+                         window_frames=4, tokens_per_frame=20)
+    log("case: fp32 D=128, S=2, W=4")
+    run_stream(shape, 7)
+
+
+def test_layer_config_sampled():
+    """The 1.3B-DiT-shaped layer: 12 heads x 128, 1560 tokens/frame, chunk 3, sink 3, window 9,
+    20 chunks; sampled query rows on fill-up, first wrap and the last chunk."""
+    shape = synth.CONFIGS["layer"]
+    log("case: layer config, 20 chunks, sampled rows")
+    rows = sample_rows(shape.n_query, 48, seed=1)
+    run_stream(shape, 20, compare={0, 1, 3, 4, 5, 19}, rows=rows, export_every=False)
+
+
+def test_value_one_gives_one_and_determinism():
+    import torch
+    shape = synth.shrink(synth.CONFIGS["layer"], heads=2, tokens_per_frame=90, window_frames=4)
+    cache = _cache(shape)
+    for c in range(5):
+        q, k, v = (t.torch("cuda") for t in synth.chunk_inputs(shape, 0, 0, c))
+        ones = torch.ones_like(v)
+        o1 = cache.attn_chunk(0, q, k, ones)
+        o2 = cache.attn_chunk(0, q, k, ones)
+        torch.cuda.synchronize()
+        if c > 0:   # history V is also 1
+            assert float((o1.float() - 1).abs().max()) <= 2 ** -7
+        assert torch.equal(o1, o2)
+        a = cache.attn_chunk(0, q, k, v)
+        b = cache.attn_chunk(0, q, k, v)
+        assert torch.equal(a, b), "attention is not deterministic"
+        cache.commit(0, k, ones)
+
+
+def test_cache_holds_copies_and_evicted_frames_do_not_leak():
+    """Poison the caller's buffers after commit and the evicted slots' old frames: the next
+    chunks' outputs still match the oracle. V carries a per-frame offset (0.05 per frame) so a
+    stale or misrouted frame shows up as a large error; the offset keeps |o| below 2, where
+    bf16 output rounding (half an ulp) stays under the 1e-2 max-abs bound."""
+    import torch
+    shape = synth.shrink(synth.CONFIGS["layer"], heads=2, tokens_per_frame=64, window_frames=3)
+    cache = _cache(shape)
+    model = _model(shape)
+    for c in range(8):
+        q, k, v = synth.chunk_inputs(shape, 0, 0, c, v_frame_offset=0.05)
+        tq, tk, tv = q.torch("cuda"), k.torch("cuda"), v.torch("cuda")
+        o = cache.attn_chunk(0, tq, tk, tv)
+        assert_close(to_np(o), model.attn_chunk(q.values, k.values, v.values), "bf16", f"chunk {c}")
+        cache.commit(0, tk, tv)
+        model.commit(k.values, v.values)
+        tk.fill_(float("nan"))
+        tv.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+
+def test_kv_quant_exhaustive_bit_exact():
+    """Every finite bf16 pattern in blocks whose max drives each scale byte 0..252."""
+    import torch
+    from windowed_attention_kv_amd import kv_quant
+    p = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pats = p[((p >> 7) & 0xFF) != 0xFF]
+    mags = pats & 0x7FFF
+    blocks = []
+    for field in range(0, 255, 1):
+        driver = np.uint16((field << 7) | 0x7F) if field > 0 else np.uint16(0x7F)
+        fit = pats[mags <= driver]
+        n_blk = -(-fit.size // 15)
+        body = np.zeros(n_blk * 15, np.uint16)
+        body[:fit.size] = fit
+        blocks.append(np.concatenate([np.full((n_blk, 1), driver, np.uint16),
+                                      body.reshape(n_blk, 15)], axis=1))
+    x = np.concatenate(blocks)                    # [blocks, 16]
+    log(f"case: kv_quant on {x.size} elements")
+    t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    pk, sc = kv_quant(t)
+    wp, ws = ofp4.quantize(x)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ws)
+    np.testing.assert_array_equal(pk.cpu().numpy(), wp)
+
+
+def test_kv_quant_random_and_ragged_rows():
+    import torch
+    from windowed_attention_kv_amd import kv_quant
+    for rows, L in ((1, 16), (7, 48), (1000, 128), (12 * 1560, 128)):
+        x = synth.bf16_matrix(rows, L, seed=rows + L)
+        t = torch.from_numpy(x.bits.view(np.int16)).view(torch.bfloat16).cuda()
+        pk, sc = kv_quant(t)
+        wp, ws = ofp4.quantize(x.bits)
+        np.testing.assert_array_equal(pk.cpu().numpy(), wp)
+        np.testing.assert_array_equal(sc.cpu().numpy(), ws)
+
+
+def test_fp4_stream():
+    shape = synth.shrink(synth.CONFIGS["layer"], name="fp4-small", heads=2, tokens_per_frame=100,
+                         window_frames=5)
+    log("case: FP4 KV stream, small")
+    run_stream(shape, 8, kv_format="fp4")
+
+
+def test_fp4_layer_config_sampled():
+    shape = synth.CONFIGS["layer"]
+    log("case: FP4 KV at the layer config, sampled rows")
+    rows = sample_rows(shape.n_query, 32, seed=2)
+    run_stream(shape, 7, kv_format="fp4", compare={0, 4, 6}, rows=rows, export_every=False)
+
+
+def _recache_case(shape, n_chunks, n_text, kv_format="dense", rows=None, after=2):
+    cache, model = run_stream(shape, n_chunks, kv_format=kv_format, compare=set(),
+                              export_every=False)
+    n = len(model.held()) * shape.tokens_per_frame
+    ins = synth.recache_inputs(shape, 0, n, n_text)
+    q, k, v, qx, kt, vt = ins
+    o, ox = cache.recache(0, *(t.torch("cuda") for t in ins))
+    ref_o, ref_ox = model.recache(q.values, k.values, v.values, qx.values, kt.values, vt.values,
+                                  k.bits, v.bits, rows=rows)
+    r = rows if rows is not None else np.arange(n)
+    assert_close(to_np(o)[r], ref_o, shape.dtype, "recache self")
+    assert_close(to_np(ox)[r], ref_ox, shape.dtype, "recache cross")
+    _check_export(cache, model, shape)
+    # later chunks see the recached values
+    rc = r[r < shape.n_query]
+    for c in range(n_chunks, n_chunks + after):
+        qq, kk, vv = synth.chunk_inputs(shape, 0, 0, c, salt=7)
+        tk, tv = kk.torch("cuda"), vv.torch("cuda")
+        oo = cache.attn_chunk(0, qq.torch("cuda"), tk, tv)
+        assert_close(to_np(oo)[rc], model.attn_chunk(qq.values, kk.values, vv.values, rows=rc),
+                     shape.dtype, f"after recache chunk {c}")
+        cache.commit(0, tk, tv)
+        model.commit(kk.values, vv.values, kk.bits, vv.bits)
+
+
+@pytest.mark.parametrize("n_chunks", [1, 3, 10])
+def test_recache_small(n_chunks):
+    shape = synth.shrink(synth.CONFIGS["layer"], name="recache-small", heads=2,
+                         tokens_per_frame=100)
+    log(f"case: recache after {n_chunks} chunks")
+    _recache_case(shape, n_chunks, n_text=77)
+
+
+def test_recache_fp32_and_fp4():
+    log("case: recache fp32 tiny")
+    _recache_case(synth.CONFIGS["tiny"], 9, n_text=20)
+    shape = synth.shrink(synth.CONFIGS["layer"], name="recache-fp4", heads=2, tokens_per_frame=64)
+    log("case: recache fp4")
+    _recache_case(shape, 5, n_text=64, kv_format="fp4")
+
+
+def test_recache_config_sampled():
+    """Recache at the prompt-switch shape: 12 held frames (18720 rows), 512 text tokens."""
+    shape = synth.CONFIGS["recache"]
+    log("case: recache config, sampled rows")
+    rows = sample_rows(12 * shape.tokens_per_frame, 40, seed=3)
+    _recache_case(shape, 10, n_text=512, rows=rows, after=1)

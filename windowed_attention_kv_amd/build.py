@@ -1,0 +1,61 @@
+"""Build the HIP library (libll.so, gfx950) and the CPU-only recording variant
+(libll_fake.so) in-tree. Run `python -m windowed_attention_kv_amd.build`."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+HIP_SOURCES = ["attn_bf16.hip", "attn_f32.hip", "cache_ops.hip"]
+HOST_SOURCES = ["ll_host.cpp"]
+LIB = os.path.join(PKG, "libll.so")
+FAKE_LIB = os.path.join(PKG, "libll_fake.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# packed-fp32 VALU ops are disabled for every HIP object (hipcc emits them on its own from
+# scalar or float2 code otherwise)
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(" ".join(cmd) + "\n" + r.stdout)
+        raise RuntimeError(f"build step failed: {cmd[0]} ({r.returncode})")
+    return r.stdout
+
+
+def build(verbose: bool = False) -> None:
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        out = _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        if verbose and out.strip():
+            print(out)
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    shutil.move(tmp, LIB)
+    # CPU-only library with the recording launch backend
+    tmp = FAKE_LIB + ".tmp"
+    _run(["g++", *HOST_FLAGS, "-shared", os.path.join(CSRC, "ll_host.cpp"),
+          os.path.join(CSRC, "fake_launch.cpp"), "-o", tmp])
+    shutil.move(tmp, FAKE_LIB)
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print("built", LIB, FAKE_LIB)

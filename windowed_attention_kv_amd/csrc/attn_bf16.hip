@@ -1,0 +1,441 @@
+// Window+sink chunk attention, bf16 in / fp32 accumulate / bf16 out, for gfx950 (MI355X).
+//
+// What it computes ("LongLive" summary page, 方法 §3 高效长推理, and 方法 §1 KV 重缓存 for the
+// recache prefill and its prompt cross-attention): for every head h and query row i
+//   o[i,h,:] = sum_j softmax_j(scale * q[i,h,:] . k[j,h,:]) v[j,h,:]
+// over the keys j visible to row i. The keys come from two segments read back to back: the
+// layer's filled cache slots (head-major, optionally FP4 e2m1/e8m0) and the call's own K/V
+// (token-major bf16). Visibility is either "all keys" (chunk attention, cross-attention) or
+// the block-causal limit of the recache prefill (launch.h, Visibility).
+//
+// Design (MI355X-first, not a port of any listed design):
+//  * one workgroup = NW waves x 32 query rows of one head; a wave keeps its 32 rows of Q in
+//    registers as the B operand of v_mfma_f32_32x32x16_bf16 and computes S^T = K Q^T, so each
+//    lane owns ONE query row: row max / row sum are in-lane reductions plus one
+//    v_permlane32_swap, never a cross-lane tree;
+//  * P^T goes straight from the S accumulator into the B operand of O^T = V^T P^T (no LDS
+//    round trip); V^T is read from LDS where the tile is stored transposed, with the keys of
+//    each 16-key group permuted so that one 16-byte read gives a lane its 8 keys;
+//  * K and V tiles of 64 keys are staged through LDS, double-buffered, one barrier per tile,
+//    with XOR-swizzled 16-byte columns; global loads are 16-byte (dense) and coalesced;
+//  * FP4 cache tiles are dequantised exactly while being written to LDS, so the MFMA inner
+//    loop is identical for both cache formats ("LongLive 2.0" distributed-inference page,
+//    NVFP4 and KV cache section: fused dequantisation);
+//  * online softmax in the exp2 domain with a lazy rescale: the running max only moves when a
+//    tile's max exceeds it by more than 2^8, so the O rescale (64 multiplies per lane) is
+//    rare; softmax is shift-invariant, so this changes rounding only;
+//  * workgroups are mapped so that each XCD (own L2) works on a contiguous range of
+//    (head, query block) tiles: the query blocks of one head share their K/V in one L2.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.h"
+
+namespace ll {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int BN = 64;          // keys per tile
+constexpr float kLazyRescale = 8.0f;  // log2 of the largest allowed p before a rescale
+
+struct DevSeg {
+  const uint8_t* k;   // dense: bf16 base; fp4: packed base
+  const uint8_t* v;
+  const uint8_t* ks;  // fp4 scales
+  const uint8_t* vs;
+  int64_t head_stride;  // elements
+  int64_t row_stride;   // elements
+  int32_t n;
+  int32_t fp4;
+};
+
+struct Params {
+  const uint16_t* q;
+  uint16_t* o;
+  int64_t q_row;     // elements between query rows (H * D)
+  int32_t H, nq, n_qblk, n_wg;
+  DevSeg a, b;
+  int32_t vis_mode, vT, vC, v_nsink;
+  int64_t v_base, v_F;
+  float c;           // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Key limit of query row `row` (keys j < limit are visible).
+__device__ __forceinline__ int32_t row_limit(const Params& p, int32_t row) {
+  const int32_t total = p.a.n + p.b.n;
+  if (p.vis_mode == 0) return total;
+  const int32_t r = row / p.vT;
+  const int64_t f = r < p.v_nsink ? int64_t(r) : p.v_base + (r - p.v_nsink);
+  const int64_t X = (f / p.vC + 1) * p.vC;
+  const int64_t ns = X < p.v_nsink ? X : int64_t(p.v_nsink);
+  const int64_t top = X < p.v_F ? X : p.v_F;
+  const int64_t nr = top > p.v_base ? top - p.v_base : 0;
+  return int32_t((ns + nr) * p.vT);
+}
+
+// FP4 -> bf16 for the 8 codes of one 32-bit word (element e in bits 4e..4e+3) with scale
+// byte sb: value = (-1)^s * grid[code & 7] * 2^(sb-127), grid = {0,.5,1,1.5,2,3,4,6}, using
+// gfx950's scaled fp4->bf16 conversion (exact: every such value is a bf16, subnormals
+// included; checked for all 256 bytes x 255 scale bytes).
+__device__ __forceinline__ uint4 dequant8(uint32_t w, uint32_t sb) {
+  const float scale = __uint_as_float(sb ? (sb << 23) : 0x00400000u);
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3)));
+}
+
+template <int D, int NW>
+struct Cfg {
+  static constexpr int NT = NW * 64;           // threads
+  static constexpr int NDC = D / 8;            // 16-byte columns per key row
+  static constexpr int NKG = NT / NDC;         // key groups per tile pass
+  static constexpr int KPT = BN / NKG;         // keys per thread per tile
+  static_assert(KPT == 1 || KPT == 2 || KPT == 4, "unsupported staging split");
+  static constexpr int K_BYTES = BN * D * 2;   // one K tile  [BN][D]
+  static constexpr int VT_BYTES = D * BN * 2;  // one V^T tile [D][BN]
+  static constexpr int BUF = K_BYTES + VT_BYTES;
+  static constexpr int LDS = 2 * BUF;
+};
+
+// swizzled byte offset of 16-byte column `c` of K row `key`
+template <int D>
+__device__ __forceinline__ int k_off(int key, int c) {
+  return key * (D * 2) + ((c ^ (key & 7)) << 4);
+}
+// swizzled byte offset of 16-byte column `c` of V^T row `d` (64 keys = 8 columns per row)
+__device__ __forceinline__ int vt_off(int d, int c) {
+  return d * (BN * 2) + ((c ^ ((d ^ (d >> 3)) & 7)) << 4);
+}
+// position of key k inside its 16-key group in the V^T tile: 4-key quads 0,1,2,3 -> 0,2,1,3
+__device__ __forceinline__ int vt_pos(int k) {
+  const int a = (k >> 2) & 3;
+  const int ap = ((a & 1) << 1) | (a >> 1);
+  return (k & ~15) | (ap << 2) | (k & 3);
+}
+
+template <int D, int NW, bool FP4>
+struct Stage {
+  using C = Cfg<D, NW>;
+  uint4 kr[C::KPT], vr[C::KPT];
+  uint32_t kw[C::KPT], vw[C::KPT], ksb[C::KPT], vsb[C::KPT];
+  bool q4[C::KPT];
+
+  __device__ __forceinline__ void load(const Params& p, int h, int tile, int dc, int kg) {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int j = tile * BN + kg * C::KPT + i;
+      kr[i] = vr[i] = make_uint4(0, 0, 0, 0);
+      q4[i] = false;
+      if (j < p.a.n) {
+        const int64_t e = h * p.a.head_stride + int64_t(j) * p.a.row_stride + dc * 8;
+        if (FP4) {
+          q4[i] = true;
+          kw[i] = *reinterpret_cast<const uint32_t*>(p.a.k + e / 2);
+          vw[i] = *reinterpret_cast<const uint32_t*>(p.a.v + e / 2);
+          ksb[i] = p.a.ks[e / 16];
+          vsb[i] = p.a.vs[e / 16];
+        } else {
+          kr[i] = *reinterpret_cast<const uint4*>(p.a.k + e * 2);
+          vr[i] = *reinterpret_cast<const uint4*>(p.a.v + e * 2);
+        }
+      } else if (j < p.a.n + p.b.n) {
+        const int64_t e = h * p.b.head_stride + int64_t(j - p.a.n) * p.b.row_stride + dc * 8;
+        kr[i] = *reinterpret_cast<const uint4*>(p.b.k + e * 2);
+        vr[i] = *reinterpret_cast<const uint4*>(p.b.v + e * 2);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* buf, int dc, int kg) {
+    uint8_t* kt = buf;
+    uint8_t* vt = buf + C::K_BYTES;
+    if (FP4) {
+#pragma unroll
+      for (int i = 0; i < C::KPT; ++i) {
+        if (q4[i]) {
+          kr[i] = dequant8(kw[i], ksb[i]);
+          vr[i] = dequant8(vw[i], vsb[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int key = kg * C::KPT + i;
+      *reinterpret_cast<uint4*>(kt + k_off<D>(key, dc)) = kr[i];
+    }
+    // V: transpose KPT keys x 8 dims in registers, write 8 rows of V^T
+    const int pos = vt_pos(kg * C::KPT);
+    const int col = pos >> 3, sub = (pos & 7) * 2;
+    const uint32_t* w[C::KPT];
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) w[i] = reinterpret_cast<const uint32_t*>(&vr[i]);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const int d = dc * 8 + dd;
+      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+      uint8_t* dst = vt + vt_off(d, col) + sub;
+      if constexpr (C::KPT == 4) {
+        uint2 x;
+        x.x = __builtin_amdgcn_perm(w[1][dd >> 1], w[0][dd >> 1], sel);
+        x.y = __builtin_amdgcn_perm(w[3][dd >> 1], w[2][dd >> 1], sel);
+        *reinterpret_cast<uint2*>(dst) = x;
+      } else if constexpr (C::KPT == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(w[1][dd >> 1], w[0][dd >> 1], sel);
+      } else {
+        const uint32_t x = w[0][dd >> 1];
+        *reinterpret_cast<uint16_t*>(dst) = uint16_t((dd & 1) ? (x >> 16) : (x & 0xFFFF));
+      }
+    }
+  }
+};
+
+template <int D, int NW, bool FP4>
+__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
+  using C = Cfg<D, NW>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  // XCD-aware tile order: workgroup ids are dealt round-robin over the 8 XCDs; give each XCD
+  // a contiguous range of tiles so neighbouring query blocks of a head share an L2.
+  const int G = p.n_wg;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int qd = G >> 3, rm = G & 7;
+  const int tile_id = (xcd < rm ? xcd * (qd + 1) : rm * (qd + 1) + (xcd - rm) * qd) + idx;
+  const int h = tile_id / p.n_qblk;
+  // heavy-first inside a head: later query blocks see more keys under the block-causal mask
+  const int qblk = p.n_qblk - 1 - (tile_id % p.n_qblk);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int row0 = qblk * (NW * 32);
+  const int row = row0 + wave * 32 + l32;            // this lane's query row
+  const int lrow = row < p.nq ? row : p.nq - 1;
+  const int lim = row_limit(p, lrow);
+  const int wave_first = min(row0 + wave * 32, p.nq - 1);
+  const int wave_min_lim = row_limit(p, wave_first);
+  const int kend = row_limit(p, min(row0 + NW * 32 - 1, p.nq - 1));
+  const int ntiles = (kend + BN - 1) / BN;
+
+  // Q^T as the MFMA B operand: lane (n = l32, khalf = hi) holds q[row][16s + 8hi .. +7]
+  bf16x8_t qreg[D / 16];
+  {
+    const uint16_t* qp = p.q + int64_t(row < p.nq ? row : 0) * p.q_row + h * D + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      uint4 x = row < p.nq ? *reinterpret_cast<const uint4*>(qp + 16 * s) : make_uint4(0, 0, 0, 0);
+      qreg[s] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16_t{};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+
+  const int dc = tid % C::NDC, kg = tid / C::NDC;
+  Stage<D, NW, FP4> st;
+  st.load(p, h, 0, dc, kg);
+  st.store(smem, dc, kg);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) st.load(p, h, t + 1, dc, kg);
+    const uint8_t* kt = smem + (t & 1) * C::BUF;
+    const uint8_t* vt = kt + C::K_BYTES;
+
+    // S^T[key][query] for two 32-key blocks
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16_t{};
+      const int key = kb * 32 + l32;
+#pragma unroll
+      for (int ss = 0; ss < D / 16; ++ss) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + k_off<D>(key, 2 * ss + hi));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ss], s[kb], 0, 0, 0);
+      }
+    }
+
+    // mask keys beyond this row's limit (only on tiles that reach past the wave's smallest)
+    const int key0 = t * BN;
+    if (key0 + BN > wave_min_lim) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= lim) s[kb][r] = -__builtin_inff();
+        }
+    }
+
+    // row max: in-lane over 32 values, then across the two lane halves of the same row
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mt = mx * p.c;
+    if (mt > m_run + kLazyRescale) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+      m_run = mt;
+    }
+
+    // P^T = exp2(c*s - m), straight into the B operand of the PV product
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -m_run));
+        l_run += e[r];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint4 u;
+        u.x = pack_bf16x2(e[8 * j + 0], e[8 * j + 1]);
+        u.y = pack_bf16x2(e[8 * j + 2], e[8 * j + 3]);
+        u.z = pack_bf16x2(e[8 * j + 4], e[8 * j + 5]);
+        u.w = pack_bf16x2(e[8 * j + 6], e[8 * j + 7]);
+        pb[kb][j] = __builtin_bit_cast(bf16x8_t, u);
+      }
+    }
+
+    // O^T[d][query] += V^T[d][key] P^T[key][query]
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = db * 32 + l32;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt + vt_off(d, 4 * kb + 2 * j + hi));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][j], oacc[db], 0, 0, 0);
+        }
+    }
+
+    if (t + 1 < ntiles) st.store(smem + ((t + 1) & 1) * C::BUF, dc, kg);
+    __syncthreads();
+  }
+
+  // epilogue: combine the two half-row sums, normalise, store bf16
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                     false, false);
+    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (row < p.nq) {
+    const float inv = 1.0f / l_run;
+    uint16_t* op = p.o + int64_t(row) * p.q_row + h * D + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 u;
+        u.x = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+        u.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(op + db * 32 + 8 * g) = u;
+      }
+  }
+}
+
+template <int D, int NW, bool FP4>
+int launch_t(const Params& p, int grid, hipStream_t stream, char* err) {
+  using C = Cfg<D, NW>;
+  auto kern = attn_bf16_kernel<D, NW, FP4>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess) {
+      snprintf(err, 256, "cannot set %d bytes of LDS", C::LDS);
+      return 1;
+    }
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(err, 256, "%s", hipGetErrorString(e));
+    return 1;
+  }
+  return 0;
+}
+
+}  // namespace
+
+int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
+  constexpr int NW = 4;
+  Params p{};
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.o = static_cast<uint16_t*>(a.o);
+  p.q_row = int64_t(a.H) * a.D;
+  p.H = a.H;
+  p.nq = a.nq;
+  const DevSeg* dummy = nullptr;
+  (void)dummy;
+  auto seg = [](const KeySeg& s) {
+    DevSeg d{};
+    d.k = static_cast<const uint8_t*>(s.k);
+    d.v = static_cast<const uint8_t*>(s.v);
+    d.ks = s.k_scales;
+    d.vs = s.v_scales;
+    d.head_stride = s.head_stride;
+    d.row_stride = s.row_stride;
+    d.n = s.n;
+    d.fp4 = s.fp4;
+    return d;
+  };
+  p.a = seg(a.seg[0]);
+  p.b = seg(a.seg[1]);
+  if (p.b.fp4) {
+    snprintf(err, 256, "only the first key segment may be FP4");
+    return 1;
+  }
+  p.vis_mode = a.vis.mode;
+  p.vT = a.vis.T;
+  p.vC = a.vis.C;
+  p.v_nsink = a.vis.n_sink;
+  p.v_base = a.vis.base;
+  p.v_F = a.vis.F;
+  p.c = a.scale * 1.4426950408889634f;
+  if (a.nq <= 0) return 0;
+  if (p.a.n + p.b.n <= 0) {
+    snprintf(err, 256, "attention over zero keys");
+    return 1;
+  }
+  p.n_qblk = (a.nq + NW * 32 - 1) / (NW * 32);
+  p.n_wg = p.n_qblk * a.H;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp4 = p.a.fp4 != 0;
+  if (a.D == 128) {
+    return fp4 ? launch_t<128, NW, true>(p, p.n_wg, s, err) : launch_t<128, NW, false>(p, p.n_wg, s, err);
+  }
+  if (a.D == 64) {
+    return fp4 ? launch_t<64, NW, true>(p, p.n_wg, s, err) : launch_t<64, NW, false>(p, p.n_wg, s, err);
+  }
+  snprintf(err, 256, "head_dim %d", a.D);
+  return 1;
+}
+
+}  // namespace ll

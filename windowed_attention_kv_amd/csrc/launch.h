@@ -1,0 +1,98 @@
+// Internal interface between the C-ABI host layer (ll_host.cpp) and the kernel launchers.
+// Plain C++ structs with no HIP types, so the host layer also builds against a recording
+// backend (fake_launch.cpp) for CPU-only tests of its validation and slot arithmetic.
+#pragma once
+
+#include <cstdint>
+
+namespace ll {
+
+// One key segment of an attention call. Key j of head h lives at
+//   dense: base + h * head_stride + j * row_stride        (elements of the call dtype)
+//   fp4  : packed + (h * head_stride + j * row_stride) / 2 bytes,
+//          scales + (h * head_stride + j * row_stride) / 16 bytes
+struct KeySeg {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const uint8_t* k_scales = nullptr;  // fp4 only
+  const uint8_t* v_scales = nullptr;  // fp4 only
+  int64_t head_stride = 0;
+  int64_t row_stride = 0;
+  int32_t n = 0;                      // keys in the segment
+  int32_t fp4 = 0;
+};
+
+// Visibility of keys to query row i (keys are indexed across seg[0] then seg[1]):
+//   mode 0: every key is visible;
+//   mode 1 (block-causal over held frames): row i is in the held frame of rank r = i / T,
+//     frame fr(r) = r < n_sink ? r : base + (r - n_sink); with X = (fr / C + 1) * C the key
+//     limit is T * (min(n_sink, X) + max(0, min(F, X) - base)); keys j < limit are visible.
+struct Visibility {
+  int32_t mode = 0;
+  int32_t T = 0, C = 0, n_sink = 0;
+  int64_t base = 0, F = 0;
+};
+
+struct AttnArgs {
+  int32_t dtype = 0;        // 0 f32, 1 bf16
+  int32_t H = 0, D = 0;
+  const void* q = nullptr;  // [nq, H, D] token-major
+  void* o = nullptr;        // [nq, H, D]
+  int32_t nq = 0;
+  KeySeg seg[2];
+  Visibility vis;
+  float scale = 0.f;
+};
+
+// Copy (or FP4-quantise) frames of a [n_frames*T, H, D] token-major K/V pair into cache
+// slots. Source frame r goes to slot slot_of_rank(r):
+//   r < n_lead ? lead_slot0 + r : S + (first_ring + r - n_lead) mod W
+// (the lead frames are sink frames, the rest rotate through the window ring).
+struct ScatterArgs {
+  int32_t dtype = 0;
+  int32_t fp4 = 0;
+  int32_t H = 0, D = 0, T = 0;
+  int32_t n_frames = 0;
+  int32_t n_lead = 0, lead_slot0 = 0;
+  int32_t S = 0, W = 0;
+  int64_t first_ring = 0;   // (frame - S) of the first non-lead frame
+  const void* k_src = nullptr;
+  const void* v_src = nullptr;
+  // destination: head-major planes [H][slots*T][D] (dense) or packed/scales (fp4)
+  void* k_dst = nullptr;
+  void* v_dst = nullptr;
+  uint8_t* k_dst_scales = nullptr;
+  uint8_t* v_dst_scales = nullptr;
+  int32_t slots = 0;
+};
+
+struct QuantArgs {
+  const void* x = nullptr;
+  int64_t rows = 0;
+  int32_t row_len = 0;
+  uint8_t* packed = nullptr;
+  uint8_t* scales = nullptr;
+};
+
+// Export head-major cache planes into slot-order token-major arrays.
+struct ExportArgs {
+  int32_t dtype = 0, fp4 = 0;
+  int32_t H = 0, D = 0, T = 0, slots = 0;
+  const void* k_src = nullptr;
+  const void* v_src = nullptr;
+  const uint8_t* k_src_scales = nullptr;
+  const uint8_t* v_src_scales = nullptr;
+  void* k_out = nullptr;
+  void* v_out = nullptr;
+  uint8_t* k_out_scales = nullptr;
+  uint8_t* v_out_scales = nullptr;
+};
+
+// Each launcher returns 0 on success or a nonzero code, with a message in `err`
+// (at least 256 bytes).
+int launch_attention(const AttnArgs& a, void* stream, char* err);
+int launch_scatter(const ScatterArgs& a, void* stream, char* err);
+int launch_quant(const QuantArgs& a, void* stream, char* err);
+int launch_export(const ExportArgs& a, void* stream, char* err);
+
+}  // namespace ll

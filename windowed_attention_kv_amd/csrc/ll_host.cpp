@@ -1,0 +1,411 @@
+// C-ABI host layer: descriptor validation, device-memory layout, per-layer ring metadata and
+// kernel launch plumbing. Nothing here touches device memory; every device operation is an
+// enqueue through launch.h.
+//
+// Cache model ("LongLive" summary page, 方法 §3 高效长推理): each layer holds S sink slots
+// (frames 0..S-1, pinned for good) and W window slots that rotate, so its size depends only
+// on S + W. Frame f sits in slot f (f < S) or S + (f - S) mod W. With F frames committed the
+// held frames are {f < min(F,S)} U [max(S, F-W), F) and the filled slots are always the prefix
+// [0, min(F,S) + min(max(F-S,0), W)), which is what lets one attention kernel read the cache
+// as a single contiguous key range per head.
+//
+// Device memory layout (per layer, K then V; each plane 256-byte aligned):
+//   dense: [H][(S+W)*T][D] elements of the dtype (head-major, so one head's keys are contiguous)
+//   fp4  : packed [H][(S+W)*T][D/2] bytes, then scales [H][(S+W)*T][D/16] bytes
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/ll.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ll_status fail(ll_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ll_status fail(ll_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ll_status ok() {
+  g_err[0] = 0;
+  return LL_OK;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t k_off, v_off, ks_off, vs_off;  // byte offsets inside one layer
+  size_t layer_bytes;
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+ll_status check_desc(const ll_cache_desc* d) {
+  if (!d) return fail(LL_EINVAL, "desc is NULL");
+  if (d->abi_version != LL_ABI_VERSION)
+    return fail(LL_EINVAL, "abi_version %u, library is %u", d->abi_version, LL_ABI_VERSION);
+  if (d->num_layers < 1 || d->num_layers > 4096) return fail(LL_EINVAL, "num_layers %d", d->num_layers);
+  if (d->num_heads < 1 || d->num_heads > 1024) return fail(LL_EINVAL, "num_heads %d", d->num_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(LL_EUNSUPPORTED, "head_dim %d (64 or 128)", d->head_dim);
+  if (d->tokens_per_frame < 1) return fail(LL_EINVAL, "tokens_per_frame %d", d->tokens_per_frame);
+  if (d->chunk_frames < 1) return fail(LL_EINVAL, "chunk_frames %d", d->chunk_frames);
+  if (d->sink_frames < 0) return fail(LL_EINVAL, "sink_frames %d", d->sink_frames);
+  if (d->window_frames < 1) return fail(LL_EINVAL, "window_frames %d", d->window_frames);
+  if (d->dtype != LL_F32 && d->dtype != LL_BF16) return fail(LL_EINVAL, "dtype %d", d->dtype);
+  if (d->kv_format != LL_KV_DENSE && d->kv_format != LL_KV_FP4)
+    return fail(LL_EINVAL, "kv_format %d", d->kv_format);
+  if (d->kv_format == LL_KV_FP4 && d->dtype != LL_BF16)
+    return fail(LL_EUNSUPPORTED, "the FP4 KV store needs bf16 tensors");
+  // key indices and per-head element offsets must fit the kernels' 32-bit key counters
+  const int64_t slots = int64_t(d->sink_frames) + d->window_frames;
+  const int64_t cache_keys = slots * d->tokens_per_frame;
+  const int64_t own_keys = int64_t(d->chunk_frames) * d->tokens_per_frame;
+  if (slots > 4096 || cache_keys + own_keys > (int64_t(1) << 30))
+    return fail(LL_EINVAL, "too many keys per head (%lld cache + %lld chunk)",
+                (long long)cache_keys, (long long)own_keys);
+  if (!(d->softmax_scale <= 0.f) && !std::isfinite(d->softmax_scale))
+    return fail(LL_EINVAL, "softmax_scale is not finite");
+  return LL_OK;
+}
+
+Layout layout_of(const ll_cache_desc* d) {
+  const size_t slots = size_t(d->sink_frames) + d->window_frames;
+  const size_t elems = slots * d->tokens_per_frame * d->num_heads * d->head_dim;
+  Layout L{};
+  if (d->kv_format == LL_KV_FP4) {
+    const size_t pk = round_up(elems / 2), sc = round_up(elems / 16);
+    L.k_off = 0;
+    L.ks_off = pk;
+    L.v_off = pk + sc;
+    L.vs_off = 2 * pk + sc;
+    L.layer_bytes = 2 * (pk + sc);
+  } else {
+    const size_t es = d->dtype == LL_BF16 ? 2 : 4;
+    const size_t pl = round_up(elems * es);
+    L.k_off = 0;
+    L.v_off = pl;
+    L.ks_off = L.vs_off = 0;
+    L.layer_bytes = 2 * pl;
+  }
+  return L;
+}
+
+}  // namespace
+
+struct ll_cache {
+  ll_cache_desc d;
+  Layout L;
+  uint8_t* mem;
+  size_t bytes;
+  float scale;
+  std::vector<int64_t> frames;  // frames committed per layer
+};
+
+namespace {
+
+int32_t slots_of(const ll_cache* c) { return c->d.sink_frames + c->d.window_frames; }
+
+int64_t n_sink_held(int64_t F, int64_t S) { return F < S ? F : S; }
+int64_t ring_base(int64_t F, int64_t S, int64_t W) { return F - W > S ? F - W : S; }
+int64_t held_count(int64_t F, int64_t S, int64_t W) {
+  const int64_t w = F - ring_base(F, S, W);
+  return n_sink_held(F, S) + (w > 0 ? w : 0);
+}
+
+uint8_t* plane(const ll_cache* c, int layer, size_t off) {
+  return c->mem + size_t(layer) * c->L.layer_bytes + off;
+}
+
+ll_status check_layer(const ll_cache* c, int32_t layer) {
+  if (!c) return fail(LL_EINVAL, "cache handle is NULL");
+  if (layer < 0 || layer >= c->d.num_layers)
+    return fail(LL_EINVAL, "layer %d out of range [0, %d)", layer, c->d.num_layers);
+  return LL_OK;
+}
+
+ll_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(LL_EINVAL, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(LL_EINVAL, "%s is not 16-byte aligned", name);
+  return LL_OK;
+}
+
+ll_status device_status(int rc, const char* what, const char* msg) {
+  if (rc == 0) return LL_OK;
+  return fail(LL_EDEVICE, "%s: %s", what, msg);
+}
+
+// Key segment over the cache's filled slot prefix of one layer.
+ll::KeySeg cache_segment(const ll_cache* c, int32_t layer) {
+  const ll_cache_desc& d = c->d;
+  const int64_t F = c->frames[layer];
+  const int64_t nvalid = n_sink_held(F, d.sink_frames) +
+                         std::min<int64_t>(std::max<int64_t>(F - d.sink_frames, 0), d.window_frames);
+  ll::KeySeg s;
+  s.k = plane(c, layer, c->L.k_off);
+  s.v = plane(c, layer, c->L.v_off);
+  s.fp4 = d.kv_format == LL_KV_FP4;
+  if (s.fp4) {
+    s.k_scales = plane(c, layer, c->L.ks_off);
+    s.v_scales = plane(c, layer, c->L.vs_off);
+  }
+  s.head_stride = int64_t(slots_of(c)) * d.tokens_per_frame * d.head_dim;
+  s.row_stride = d.head_dim;
+  s.n = int32_t(nvalid * d.tokens_per_frame);
+  return s;
+}
+
+ll::KeySeg input_segment(const ll_cache_desc& d, const void* k, const void* v, int32_t n) {
+  ll::KeySeg s;
+  s.k = k;
+  s.v = v;
+  s.head_stride = d.head_dim;
+  s.row_stride = int64_t(d.num_heads) * d.head_dim;
+  s.n = n;
+  return s;
+}
+
+ll::ScatterArgs scatter_base(const ll_cache* c, int32_t layer) {
+  const ll_cache_desc& d = c->d;
+  ll::ScatterArgs a;
+  a.dtype = d.dtype;
+  a.fp4 = d.kv_format == LL_KV_FP4;
+  a.H = d.num_heads;
+  a.D = d.head_dim;
+  a.T = d.tokens_per_frame;
+  a.S = d.sink_frames;
+  a.W = d.window_frames;
+  a.slots = slots_of(c);
+  a.k_dst = plane(c, layer, c->L.k_off);
+  a.v_dst = plane(c, layer, c->L.v_off);
+  if (a.fp4) {
+    a.k_dst_scales = plane(c, layer, c->L.ks_off);
+    a.v_dst_scales = plane(c, layer, c->L.vs_off);
+  }
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+ll_status ll_cache_size(const ll_cache_desc* desc, size_t* device_bytes) {
+  if (ll_status s = check_desc(desc)) return s;
+  if (!device_bytes) return fail(LL_EINVAL, "device_bytes is NULL");
+  *device_bytes = layout_of(desc).layer_bytes * size_t(desc->num_layers);
+  return ok();
+}
+
+ll_status ll_cache_create(const ll_cache_desc* desc, void* device_mem, size_t device_bytes,
+                          ll_cache** out) {
+  if (ll_status s = check_desc(desc)) return s;
+  if (!out) return fail(LL_EINVAL, "out is NULL");
+  if (!device_mem) return fail(LL_EINVAL, "device_mem is NULL");
+  if (!aligned(device_mem, kAlign)) return fail(LL_EINVAL, "device_mem is not 256-byte aligned");
+  const Layout L = layout_of(desc);
+  const size_t need = L.layer_bytes * size_t(desc->num_layers);
+  if (device_bytes < need)
+    return fail(LL_EINVAL, "device_bytes %zu < required %zu", device_bytes, need);
+  ll_cache* c = new (std::nothrow) ll_cache;
+  if (!c) return fail(LL_EINVAL, "out of host memory");
+  c->d = *desc;
+  c->L = L;
+  c->mem = static_cast<uint8_t*>(device_mem);
+  c->bytes = device_bytes;
+  c->scale = desc->softmax_scale > 0.f ? desc->softmax_scale
+                                       : float(1.0 / std::sqrt(double(desc->head_dim)));
+  c->frames.assign(size_t(desc->num_layers), 0);
+  *out = c;
+  return ok();
+}
+
+ll_status ll_cache_destroy(ll_cache* cache) {
+  delete cache;
+  return ok();
+}
+
+ll_status ll_cache_reset(ll_cache* cache) {
+  if (!cache) return fail(LL_EINVAL, "cache handle is NULL");
+  std::fill(cache->frames.begin(), cache->frames.end(), 0);
+  return ok();
+}
+
+ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const void* k,
+                        const void* v, void* o, void* stream) {
+  if (ll_status s = check_layer(cache, layer)) return s;
+  if (ll_status s = check_ptr(q, "q")) return s;
+  if (ll_status s = check_ptr(k, "k")) return s;
+  if (ll_status s = check_ptr(v, "v")) return s;
+  if (ll_status s = check_ptr(o, "o")) return s;
+  const ll_cache_desc& d = cache->d;
+  const int32_t n = d.chunk_frames * d.tokens_per_frame;
+  ll::AttnArgs a;
+  a.dtype = d.dtype;
+  a.H = d.num_heads;
+  a.D = d.head_dim;
+  a.q = q;
+  a.o = o;
+  a.nq = n;
+  a.seg[0] = cache_segment(cache, layer);
+  a.seg[1] = input_segment(d, k, v, n);
+  a.scale = cache->scale;
+  char msg[256] = "";
+  return device_status(ll::launch_attention(a, stream, msg), "attention launch", msg) ?: ok();
+}
+
+ll_status ll_cache_commit(ll_cache* cache, int32_t layer, const void* k, const void* v,
+                          void* stream) {
+  if (ll_status s = check_layer(cache, layer)) return s;
+  if (ll_status s = check_ptr(k, "k")) return s;
+  if (ll_status s = check_ptr(v, "v")) return s;
+  const ll_cache_desc& d = cache->d;
+  const int64_t F = cache->frames[layer];
+  const int64_t S = d.sink_frames, C = d.chunk_frames;
+  ll::ScatterArgs a = scatter_base(cache, layer);
+  a.n_frames = d.chunk_frames;
+  a.n_lead = int32_t(std::min<int64_t>(std::max<int64_t>(S - F, 0), C));
+  a.lead_slot0 = int32_t(F < S ? F : 0);
+  a.first_ring = std::max<int64_t>(F, S) - S;
+  a.k_src = k;
+  a.v_src = v;
+  char msg[256] = "";
+  if (ll_status s = device_status(ll::launch_scatter(a, stream, msg), "commit launch", msg))
+    return s;
+  cache->frames[layer] = F + C;
+  return ok();
+}
+
+ll_status ll_recache(ll_cache* cache, int32_t layer, const void* q, const void* k,
+                     const void* v, const void* qx, const void* k_text, const void* v_text,
+                     int32_t n_text, void* o, void* ox, void* stream) {
+  if (ll_status s = check_layer(cache, layer)) return s;
+  const char* names[] = {"q", "k", "v", "qx", "k_text", "v_text", "o", "ox"};
+  const void* ptrs[] = {q, k, v, qx, k_text, v_text, o, ox};
+  for (int i = 0; i < 8; ++i)
+    if (ll_status s = check_ptr(ptrs[i], names[i])) return s;
+  if (n_text < 1 || n_text > (1 << 30)) return fail(LL_EINVAL, "n_text %d", n_text);
+  const ll_cache_desc& d = cache->d;
+  const int64_t F = cache->frames[layer];
+  const int64_t S = d.sink_frames, W = d.window_frames;
+  const int64_t held = held_count(F, S, W);
+  if (held == 0) return fail(LL_ESTATE, "recache of layer %d, which holds no frame", layer);
+  const int64_t nsink = n_sink_held(F, S), base = ring_base(F, S, W);
+  const int32_t n = int32_t(held * d.tokens_per_frame);
+  char msg[256] = "";
+
+  // (i) self-attention, block-causal over the held frames' chunks
+  ll::AttnArgs a;
+  a.dtype = d.dtype;
+  a.H = d.num_heads;
+  a.D = d.head_dim;
+  a.q = q;
+  a.o = o;
+  a.nq = n;
+  a.seg[0] = input_segment(d, k, v, n);
+  a.seg[1] = input_segment(d, k, v, 0);
+  a.vis.mode = 1;
+  a.vis.T = d.tokens_per_frame;
+  a.vis.C = d.chunk_frames;
+  a.vis.n_sink = int32_t(nsink);
+  a.vis.base = base;
+  a.vis.F = F;
+  a.scale = cache->scale;
+  if (ll_status s = device_status(ll::launch_attention(a, stream, msg), "recache attention", msg))
+    return s;
+  // (ii) cross-attention to the new prompt's text tokens
+  ll::AttnArgs x = a;
+  x.q = qx;
+  x.o = ox;
+  x.seg[0] = input_segment(d, k_text, v_text, n_text);
+  x.vis = ll::Visibility{};
+  if (ll_status s = device_status(ll::launch_attention(x, stream, msg), "recache cross-attention", msg))
+    return s;
+  // (iii) rewrite every held frame's slot with the new K/V
+  ll::ScatterArgs w = scatter_base(cache, layer);
+  w.n_frames = int32_t(held);
+  w.n_lead = int32_t(nsink);
+  w.lead_slot0 = 0;
+  w.first_ring = base - S;
+  w.k_src = k;
+  w.v_src = v;
+  if (ll_status s = device_status(ll::launch_scatter(w, stream, msg), "recache rewrite", msg))
+    return s;
+  return ok();
+}
+
+ll_status ll_kv_quant(const void* x_bf16, int64_t rows, int32_t row_len, uint8_t* packed,
+                      uint8_t* scales, void* stream) {
+  if (rows < 0) return fail(LL_EINVAL, "rows %lld", (long long)rows);
+  if (row_len <= 0 || row_len % 16) return fail(LL_EINVAL, "row_len %d (multiple of 16)", row_len);
+  if (rows == 0) return ok();
+  if (ll_status s = check_ptr(x_bf16, "x")) return s;
+  if (!packed || !scales) return fail(LL_EINVAL, "packed/scales is NULL");
+  if (rows > (int64_t(1) << 40) / row_len) return fail(LL_EINVAL, "input too large");
+  ll::QuantArgs a;
+  a.x = x_bf16;
+  a.rows = rows;
+  a.row_len = row_len;
+  a.packed = packed;
+  a.scales = scales;
+  char msg[256] = "";
+  return device_status(ll::launch_quant(a, stream, msg), "quant launch", msg) ?: ok();
+}
+
+ll_status ll_cache_state(const ll_cache* cache, int32_t layer, int64_t* frames_committed,
+                         int32_t* slot_frame) {
+  if (ll_status s = check_layer(cache, layer)) return s;
+  const int64_t F = cache->frames[layer];
+  const int64_t S = cache->d.sink_frames, W = cache->d.window_frames;
+  if (frames_committed) *frames_committed = F;
+  if (slot_frame) {
+    for (int32_t i = 0; i < slots_of(cache); ++i) slot_frame[i] = -1;
+    for (int64_t f = 0; f < n_sink_held(F, S); ++f) slot_frame[f] = int32_t(f);
+    for (int64_t f = ring_base(F, S, W); f < F; ++f) slot_frame[S + (f - S) % W] = int32_t(f);
+  }
+  return ok();
+}
+
+ll_status ll_cache_export(const ll_cache* cache, int32_t layer, void* k_out, void* v_out,
+                          uint8_t* k_scales, uint8_t* v_scales, void* stream) {
+  if (ll_status s = check_layer(cache, layer)) return s;
+  if (ll_status s = check_ptr(k_out, "k_out")) return s;
+  if (ll_status s = check_ptr(v_out, "v_out")) return s;
+  const ll_cache_desc& d = cache->d;
+  ll::ExportArgs a;
+  a.dtype = d.dtype;
+  a.fp4 = d.kv_format == LL_KV_FP4;
+  if (a.fp4 && (!k_scales || !v_scales)) return fail(LL_EINVAL, "k_scales/v_scales is NULL");
+  a.H = d.num_heads;
+  a.D = d.head_dim;
+  a.T = d.tokens_per_frame;
+  a.slots = slots_of(cache);
+  a.k_src = plane(cache, layer, cache->L.k_off);
+  a.v_src = plane(cache, layer, cache->L.v_off);
+  if (a.fp4) {
+    a.k_src_scales = plane(cache, layer, cache->L.ks_off);
+    a.v_src_scales = plane(cache, layer, cache->L.vs_off);
+  }
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.k_out_scales = k_scales;
+  a.v_out_scales = v_scales;
+  char msg[256] = "";
+  return device_status(ll::launch_export(a, stream, msg), "export launch", msg) ?: ok();
+}
+
+const char* ll_last_error(void) { return g_err; }
+
+}  // extern "C"
