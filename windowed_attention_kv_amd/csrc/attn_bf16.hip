@@ -60,8 +60,7 @@ struct Params {
   int64_t q_row;     // elements between query rows (H * D)
   int32_t H, nq, n_qblk, n_wg;
   DevSeg a, b;
-  int32_t vis_mode, vT, vC, v_nsink;
-  int64_t v_base, v_F;
+  int32_t vis_mode, vT, vC, v_nsink, v_base, v_F;
   float c;           // softmax scale * log2(e)
 };
 
@@ -70,17 +69,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Key limit of query row `row` (keys j < limit are visible).
+// Key limit of query row `row` (keys j < limit are visible). Frame ids fit 31 bits (the host
+// rejects streams beyond that).
 __device__ __forceinline__ int32_t row_limit(const Params& p, int32_t row) {
-  const int32_t total = p.a.n + p.b.n;
-  if (p.vis_mode == 0) return total;
+  if (p.vis_mode == 0) return p.a.n + p.b.n;
   const int32_t r = row / p.vT;
-  const int64_t f = r < p.v_nsink ? int64_t(r) : p.v_base + (r - p.v_nsink);
-  const int64_t X = (f / p.vC + 1) * p.vC;
-  const int64_t ns = X < p.v_nsink ? X : int64_t(p.v_nsink);
-  const int64_t top = X < p.v_F ? X : p.v_F;
-  const int64_t nr = top > p.v_base ? top - p.v_base : 0;
-  return int32_t((ns + nr) * p.vT);
+  const int32_t f = r < p.v_nsink ? r : p.v_base + (r - p.v_nsink);
+  const int32_t X = (f / p.vC + 1) * p.vC;
+  const int32_t ns = X < p.v_nsink ? X : p.v_nsink;
+  const int32_t top = X < p.v_F ? X : p.v_F;
+  const int32_t nr = top > p.v_base ? top - p.v_base : 0;
+  return (ns + nr) * p.vT;
 }
 
 // FP4 -> bf16 for the 8 codes of one 32-bit word (element e in bits 4e..4e+3) with scale
@@ -124,48 +123,119 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~15) | (ap << 2) | (k & 3);
 }
 
+// Buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes return zero, which
+// is how keys past a segment's end (and the ragged tail) are read as zeros without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+
 template <int D, int NW, bool FP4>
 struct Stage {
   using C = Cfg<D, NW>;
+  // per-head resources: segment A (cache, head-major; dense or fp4 planes) and segment B
+  // (the call's own K/V, token-major)
+  __amdgpu_buffer_rsrc_t ak, av, aks, avs, bk, bv;
+  int32_t na, a_row, b_row;   // keys in A; row strides in bytes (fp4: packed bytes)
   uint4 kr[C::KPT], vr[C::KPT];
   uint32_t kw[C::KPT], vw[C::KPT], ksb[C::KPT], vsb[C::KPT];
-  bool q4[C::KPT];
 
-  __device__ __forceinline__ void load(const Params& p, int h, int tile, int dc, int kg) {
+  __device__ __forceinline__ void init(const Params& p, int h) {
+    na = p.a.n;
+    if (FP4) {
+      a_row = int32_t(p.a.row_stride / 2);
+      const int64_t e0 = h * p.a.head_stride;
+      ak = rsrc(p.a.k + e0 / 2, uint32_t(p.a.n) * a_row);
+      av = rsrc(p.a.v + e0 / 2, uint32_t(p.a.n) * a_row);
+      aks = rsrc(p.a.ks + e0 / 16, uint32_t(p.a.n) * (a_row / 8));
+      avs = rsrc(p.a.vs + e0 / 16, uint32_t(p.a.n) * (a_row / 8));
+    } else {
+      a_row = int32_t(p.a.row_stride * 2);
+      const int64_t e0 = h * p.a.head_stride;
+      ak = rsrc(p.a.k + e0 * 2, uint32_t(p.a.n) * a_row);
+      av = rsrc(p.a.v + e0 * 2, uint32_t(p.a.n) * a_row);
+    }
+    b_row = int32_t(p.b.row_stride * 2);
+    const uint32_t bbytes = p.b.n > 0 ? uint32_t(p.b.n - 1) * b_row + D * 2 : 0u;
+    bk = rsrc(p.b.k + h * p.b.head_stride * 2, bbytes);
+    bv = rsrc(p.b.v + h * p.b.head_stride * 2, bbytes);
+  }
+
+  __device__ __forceinline__ void load_a(int j0, int dc) {
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
-      const int j = tile * BN + kg * C::KPT + i;
-      kr[i] = vr[i] = make_uint4(0, 0, 0, 0);
-      q4[i] = false;
-      if (j < p.a.n) {
-        const int64_t e = h * p.a.head_stride + int64_t(j) * p.a.row_stride + dc * 8;
-        if (FP4) {
-          q4[i] = true;
-          kw[i] = *reinterpret_cast<const uint32_t*>(p.a.k + e / 2);
-          vw[i] = *reinterpret_cast<const uint32_t*>(p.a.v + e / 2);
-          ksb[i] = p.a.ks[e / 16];
-          vsb[i] = p.a.vs[e / 16];
-        } else {
-          kr[i] = *reinterpret_cast<const uint4*>(p.a.k + e * 2);
-          vr[i] = *reinterpret_cast<const uint4*>(p.a.v + e * 2);
-        }
-      } else if (j < p.a.n + p.b.n) {
-        const int64_t e = h * p.b.head_stride + int64_t(j - p.a.n) * p.b.row_stride + dc * 8;
-        kr[i] = *reinterpret_cast<const uint4*>(p.b.k + e * 2);
-        vr[i] = *reinterpret_cast<const uint4*>(p.b.v + e * 2);
+      const int j = j0 + i;
+      if (FP4) {
+        const uint32_t off = uint32_t(j) * a_row + dc * 4;
+        kw[i] = __builtin_amdgcn_raw_buffer_load_b32(ak, off, 0, 0);
+        vw[i] = __builtin_amdgcn_raw_buffer_load_b32(av, off, 0, 0);
+        const uint32_t so = uint32_t(j) * (a_row / 8) + (dc >> 1);
+        ksb[i] = __builtin_amdgcn_raw_buffer_load_b8(aks, so, 0, 0);
+        vsb[i] = __builtin_amdgcn_raw_buffer_load_b8(avs, so, 0, 0);
+      } else {
+        const uint32_t off = uint32_t(j) * a_row + dc * 16;
+        kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ak, off, 0, 0));
+        vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(av, off, 0, 0));
       }
     }
   }
 
-  __device__ __forceinline__ void store(uint8_t* buf, int dc, int kg) {
+  // keys j0.. of segment B (j0 may be negative: those rows read as zero)
+  __device__ __forceinline__ void load_b(int j0, int dc, bool accumulate) {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const uint32_t off = uint32_t(j0 + i) * uint32_t(b_row) + dc * 16;
+      const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bk, off, 0, 0));
+      const uint4 y = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bv, off, 0, 0));
+      if (accumulate) {
+        kr[i] = make_uint4(kr[i].x | x.x, kr[i].y | x.y, kr[i].z | x.z, kr[i].w | x.w);
+        vr[i] = make_uint4(vr[i].x | y.x, vr[i].y | y.y, vr[i].z | y.z, vr[i].w | y.w);
+      } else {
+        kr[i] = x;
+        vr[i] = y;
+      }
+    }
+  }
+
+  // stage tile `tile` into registers; `mixed` marks the one tile that straddles A and B
+  __device__ __forceinline__ void load(int tile, int dc, int kg) {
+    const int t0 = tile * BN;
+    const int j0 = t0 + kg * C::KPT;
+    if (t0 + BN <= na) {
+      load_a(j0, dc);
+    } else if (t0 >= na) {
+      if (FP4) {
+#pragma unroll
+        for (int i = 0; i < C::KPT; ++i) kw[i] = vw[i] = ksb[i] = vsb[i] = 0;
+      }
+      load_b(j0 - na, dc, false);
+    } else {
+      load_a(j0, dc);
+      if (FP4) {
+#pragma unroll
+        for (int i = 0; i < C::KPT; ++i) kr[i] = vr[i] = make_uint4(0, 0, 0, 0);
+      }
+      load_b(j0 - na, dc, !FP4);
+      if (FP4) {
+        // keys of A keep their codes, keys of B their bf16 values; mark B keys with sb 0xFFFF
+#pragma unroll
+        for (int i = 0; i < C::KPT; ++i)
+          if (j0 + i >= na) ksb[i] = vsb[i] = 0xFFFFu;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* buf, int tile, int dc, int kg) {
     uint8_t* kt = buf;
     uint8_t* vt = buf + C::K_BYTES;
     if (FP4) {
+      const int t0 = tile * BN;
+      if (t0 < na) {
 #pragma unroll
-      for (int i = 0; i < C::KPT; ++i) {
-        if (q4[i]) {
-          kr[i] = dequant8(kw[i], ksb[i]);
-          vr[i] = dequant8(vw[i], vsb[i]);
+        for (int i = 0; i < C::KPT; ++i) {
+          if (ksb[i] != 0xFFFFu) {
+            kr[i] = dequant8(kw[i], ksb[i]);
+            vr[i] = dequant8(vw[i], vsb[i]);
+          }
         }
       }
     }
@@ -201,7 +271,7 @@ struct Stage {
 };
 
 template <int D, int NW, bool FP4>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   using C = Cfg<D, NW>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -247,12 +317,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
 
   const int dc = tid % C::NDC, kg = tid / C::NDC;
   Stage<D, NW, FP4> st;
-  st.load(p, h, 0, dc, kg);
-  st.store(smem, dc, kg);
+  st.init(p, h);
+  st.load(0, dc, kg);
+  st.store(smem, 0, dc, kg);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) st.load(p, h, t + 1, dc, kg);
+    if (t + 1 < ntiles) st.load(t + 1, dc, kg);
     const uint8_t* kt = smem + (t & 1) * C::BUF;
     const uint8_t* vt = kt + C::K_BYTES;
 
@@ -281,13 +352,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         }
     }
 
-    // row max: in-lane over 32 values, then across the two lane halves of the same row
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    // row max: in-lane tree over 32 values, then across the two lane halves of the same row
+    float mx;
     {
+      float t8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        t8[i] = fmaxf(fmaxf(s[0][2 * i], s[0][2 * i + 1]), fmaxf(s[1][2 * i], s[1][2 * i + 1]));
+#pragma unroll
+      for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) t8[i] = fmaxf(t8[i], t8[i + w]);
+      mx = t8[0];
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -303,13 +379,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
 
     // P^T = exp2(c*s - m), straight into the B operand of the PV product
     bf16x8_t pb[2][2];
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float e[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -m_run));
-        l_run += e[r];
+        psum[r & 3] += e[r];
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -321,6 +398,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         pb[kb][j] = __builtin_bit_cast(bf16x8_t, u);
       }
     }
+    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
 
     // O^T[d][query] += V^T[d][key] P^T[key][query]
 #pragma unroll
@@ -335,7 +413,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Params p) {
         }
     }
 
-    if (t + 1 < ntiles) st.store(smem + ((t + 1) & 1) * C::BUF, dc, kg);
+    if (t + 1 < ntiles) st.store(smem + ((t + 1) & 1) * C::BUF, t + 1, dc, kg);
     __syncthreads();
   }
 
@@ -392,8 +470,6 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
   p.q_row = int64_t(a.H) * a.D;
   p.H = a.H;
   p.nq = a.nq;
-  const DevSeg* dummy = nullptr;
-  (void)dummy;
   auto seg = [](const KeySeg& s) {
     DevSeg d{};
     d.k = static_cast<const uint8_t*>(s.k);
@@ -416,8 +492,8 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
   p.vT = a.vis.T;
   p.vC = a.vis.C;
   p.v_nsink = a.vis.n_sink;
-  p.v_base = a.vis.base;
-  p.v_F = a.vis.F;
+  p.v_base = int32_t(a.vis.base);
+  p.v_F = int32_t(a.vis.F);
   p.c = a.scale * 1.4426950408889634f;
   if (a.nq <= 0) return 0;
   if (p.a.n + p.b.n <= 0) {

@@ -77,6 +77,13 @@ ll_status check_desc(const ll_cache_desc* d) {
   if (slots > 4096 || cache_keys + own_keys > (int64_t(1) << 30))
     return fail(LL_EINVAL, "too many keys per head (%lld cache + %lld chunk)",
                 (long long)cache_keys, (long long)own_keys);
+  // the kernels address one head's cache plane, and any [rows, H, D] tensor of up to
+  // (S+W)*T rows, with 32-bit byte offsets
+  const int64_t es = d->dtype == LL_BF16 ? 2 : 4;
+  const int64_t row_bytes = int64_t(d->num_heads) * d->head_dim * es;
+  if (cache_keys * row_bytes >= (int64_t(1) << 31) || own_keys * row_bytes >= (int64_t(1) << 31))
+    return fail(LL_EUNSUPPORTED, "tensors of %lld rows x %lld bytes exceed 2 GiB",
+                (long long)std::max(cache_keys, own_keys), (long long)row_bytes);
   if (!(d->softmax_scale <= 0.f) && !std::isfinite(d->softmax_scale))
     return fail(LL_EINVAL, "softmax_scale is not finite");
   return LL_OK;
@@ -274,6 +281,9 @@ ll_status ll_cache_commit(ll_cache* cache, int32_t layer, const void* k, const v
   const ll_cache_desc& d = cache->d;
   const int64_t F = cache->frames[layer];
   const int64_t S = d.sink_frames, C = d.chunk_frames;
+  if (F + C >= (int64_t(1) << 31) - 1)
+    return fail(LL_ESTATE, "layer %d has committed %lld frames: frame ids must fit 31 bits", layer,
+                (long long)F);
   ll::ScatterArgs a = scatter_base(cache, layer);
   a.n_frames = d.chunk_frames;
   a.n_lead = int32_t(std::min<int64_t>(std::max<int64_t>(S - F, 0), C));
@@ -296,7 +306,9 @@ ll_status ll_recache(ll_cache* cache, int32_t layer, const void* q, const void* 
   const void* ptrs[] = {q, k, v, qx, k_text, v_text, o, ox};
   for (int i = 0; i < 8; ++i)
     if (ll_status s = check_ptr(ptrs[i], names[i])) return s;
-  if (n_text < 1 || n_text > (1 << 30)) return fail(LL_EINVAL, "n_text %d", n_text);
+  if (n_text < 1 || int64_t(n_text) * cache->d.num_heads * cache->d.head_dim *
+                           (cache->d.dtype == LL_BF16 ? 2 : 4) >= (int64_t(1) << 31))
+    return fail(LL_EINVAL, "n_text %d", n_text);
   const ll_cache_desc& d = cache->d;
   const int64_t F = cache->frames[layer];
   const int64_t S = d.sink_frames, W = d.window_frames;
