@@ -32,7 +32,22 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the FP4 / recache rows")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
 
 
 def visible_keys(chunk, C, S, W, T):
@@ -85,7 +100,7 @@ def run_stream(cache, inputs, timer=None):
     for c, (q, k, v) in enumerate(inputs):
         if timer:
             s = timer.start()
-        cache.attn_chunk(0, q, k, v, out=q.new_empty(q.shape) if False else _OUT[0])
+        cache.attn_chunk(0, q, k, v, out=_OUT[0])
         if timer:
             timer.stop(s, "attn")
             s = timer.start()
@@ -213,6 +228,9 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
               "multi-GPU path; the per-head sharding design is described in DESIGN.md",

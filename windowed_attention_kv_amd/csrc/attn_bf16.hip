@@ -101,18 +101,22 @@ struct Cfg {
   static constexpr int NKG = NT / NDC;         // key groups per tile pass
   static constexpr int KPT = BN / NKG;         // keys per thread per tile
   static_assert(KPT == 1 || KPT == 2 || KPT == 4, "unsupported staging split");
-  static constexpr int K_BYTES = BN * D * 2;   // one K tile  [BN][D]
+  static constexpr int KP = D * 2 + 16;        // K row pitch: 16 bytes of padding per row
+  static constexpr int K_BYTES = BN * KP;      // one K tile  [BN][D] (padded rows)
   static constexpr int VT_BYTES = D * BN * 2;  // one V^T tile [D][BN]
   static constexpr int BUF = K_BYTES + VT_BYTES;
   static constexpr int LDS = 2 * BUF;
 };
 
-// swizzled byte offset of 16-byte column `c` of K row `key`
+// K rows are padded to D*2+16 bytes: 16 consecutive rows at the same column land on 16
+// distinct 16-byte bank groups, and every read address is lane base + immediate.
 template <int D>
 __device__ __forceinline__ int k_off(int key, int c) {
-  return key * (D * 2) + ((c ^ (key & 7)) << 4);
+  return key * (D * 2 + 16) + (c << 4);
 }
-// swizzled byte offset of 16-byte column `c` of V^T row `d` (64 keys = 8 columns per row)
+// V^T rows (64 keys = 128 bytes) use an XOR swizzle of the 16-byte column by
+// (d ^ d>>3) & 7, which keeps both the transposing writes and the column reads spread
+// over the banks
 __device__ __forceinline__ int vt_off(int d, int c) {
   return d * (BN * 2) + ((c ^ ((d ^ (d >> 3)) & 7)) << 4);
 }
@@ -315,6 +319,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
+  // per-lane LDS offsets (tile-invariant): K row l32 column hi; V^T row l32 at the four
+  // (kb ^ db&1, j) column patterns
+  const int k_lane = k_off<D>(l32, hi);
+  int v_lane[4];
+#pragma unroll
+  for (int sel = 0; sel < 4; ++sel) v_lane[sel] = vt_off(l32, 4 * (sel >> 1) + 2 * (sel & 1) + hi);
+
   const int dc = tid % C::NDC, kg = tid / C::NDC;
   Stage<D, NW, FP4> st;
   st.init(p, h);
@@ -327,15 +338,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const uint8_t* kt = smem + (t & 1) * C::BUF;
     const uint8_t* vt = kt + C::K_BYTES;
 
-    // S^T[key][query] for two 32-key blocks
+    // S^T[key][query] for two 32-key blocks: lane reads K row kb*32 + l32, column 2ss + hi
     f32x16_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16_t{};
-      const int key = kb * 32 + l32;
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + k_off<D>(key, 2 * ss + hi));
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + k_lane + kb * 32 * C::KP + ss * 32);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ss], s[kb], 0, 0, 0);
       }
     }
@@ -377,38 +387,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       m_run = mt;
     }
 
-    // P^T = exp2(c*s - m), straight into the B operand of the PV product
+    // P^T = exp2(c*s - m), rounded to bf16 straight into the B operand of the PV product;
+    // the row sum adds the rounded values (v_dot2 with ones), i.e. exactly the weights the
+    // PV product uses
     bf16x8_t pb[2][2];
     float psum[4] = {0.f, 0.f, 0.f, 0.f};
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -m_run));
-        psum[r & 3] += e[r];
-      }
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -m_run));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        uint4 u;
-        u.x = pack_bf16x2(e[8 * j + 0], e[8 * j + 1]);
-        u.y = pack_bf16x2(e[8 * j + 2], e[8 * j + 3]);
-        u.z = pack_bf16x2(e[8 * j + 4], e[8 * j + 5]);
-        u.w = pack_bf16x2(e[8 * j + 6], e[8 * j + 7]);
-        pb[kb][j] = __builtin_bit_cast(bf16x8_t, u);
+        uint32_t u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u[i] = pack_bf16x2(e[8 * j + 2 * i], e[8 * j + 2 * i + 1]);
+          psum[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[i]), ones, psum[i], false);
+        }
+        pb[kb][j] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
       }
     }
     l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
 
-    // O^T[d][query] += V^T[d][key] P^T[key][query]
+    // O^T[d][query] += V^T[d][key] P^T[key][query]; lane reads V^T row db*32 + l32 at
+    // column 4kb + 2j + hi, whose swizzle depends on (kb ^ db&1, j): four lane bases
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = db * 32 + l32;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt + vt_off(d, 4 * kb + 2 * j + hi));
+          const int sel = ((kb ^ (db & 1)) << 1) | j;
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vt + v_lane[sel] + db * 32 * (BN * 2));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][j], oacc[db], 0, 0, 0);
         }
     }
