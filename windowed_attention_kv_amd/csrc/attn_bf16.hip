@@ -39,6 +39,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;          // keys per tile
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest allowed p before a rescale
@@ -274,6 +275,55 @@ struct Stage {
   }
 };
 
+// Online softmax of one 64-key tile for the lane's query row: S^T values s (2 x 16 per lane,
+// masked keys already -inf) -> bf16 weights pb (the B operand of the PV product), updating the
+// running max m (exp2 domain, scaled by c), the running sum l and, when the max moves, O.
+// The running max only moves when the tile max exceeds it by more than 2^8 (lazy rescale:
+// softmax is shift-invariant, so this only changes rounding); the row sum adds the
+// bf16-rounded weights (v_dot2 with ones), exactly the weights the PV product uses.
+template <int D>
+__device__ __forceinline__ void softmax_update(f32x16_t (&s)[2], float c, float& m_run,
+                                               float& l_run, f32x16_t (&oacc)[D / 32],
+                                               bf16x8_t (&pb)[2][2]) {
+  float t8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    t8[i] = fmaxf(fmaxf(s[0][2 * i], s[0][2 * i + 1]), fmaxf(s[1][2 * i], s[1][2 * i + 1]));
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t8[i] = fmaxf(t8[i], t8[i + w]);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t8[0]), __float_as_uint(t8[0]),
+                                                   false, false);
+  const float mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+  if (mt > m_run + kLazyRescale) {
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+    m_run = mt;
+  }
+  float psum[4] = {0.f, 0.f, 0.f, 0.f};
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_run));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u[i] = pack_bf16x2(e[8 * j + 2 * i], e[8 * j + 2 * i + 1]);
+        psum[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[i]), ones, psum[i], false);
+      }
+      pb[kb][j] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
+    }
+  }
+  l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+}
+
 template <int D, int NW, bool FP4>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(Params p) {
   using C = Cfg<D, NW>;
@@ -362,54 +412,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
     }
 
-    // row max: in-lane tree over 32 values, then across the two lane halves of the same row
-    float mx;
-    {
-      float t8[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        t8[i] = fmaxf(fmaxf(s[0][2 * i], s[0][2 * i + 1]), fmaxf(s[1][2 * i], s[1][2 * i + 1]));
-#pragma unroll
-      for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-        for (int i = 0; i < w; ++i) t8[i] = fmaxf(t8[i], t8[i + w]);
-      mx = t8[0];
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mt = mx * p.c;
-    if (mt > m_run + kLazyRescale) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-      m_run = mt;
-    }
-
-    // P^T = exp2(c*s - m), rounded to bf16 straight into the B operand of the PV product;
-    // the row sum adds the rounded values (v_dot2 with ones), i.e. exactly the weights the
-    // PV product uses
     bf16x8_t pb[2][2];
-    float psum[4] = {0.f, 0.f, 0.f, 0.f};
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.c, -m_run));
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint32_t u[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u[i] = pack_bf16x2(e[8 * j + 2 * i], e[8 * j + 2 * i + 1]);
-          psum[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[i]), ones, psum[i], false);
-        }
-        pb[kb][j] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
-      }
-    }
-    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+    softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
 
     // O^T[d][query] += V^T[d][key] P^T[key][query]; lane reads V^T row db*32 + l32 at
     // column 4kb + 2j + hi, whose swizzle depends on (kb ^ db&1, j): four lane bases
@@ -448,6 +452,225 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         *reinterpret_cast<uint2*>(op + db * 32 + 8 * g) = u;
       }
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// Dense bf16, head_dim 128: K and V tiles go global -> LDS with gfx950's direct-to-LDS buffer
+// loads (no staging registers, no transposing writes). V stays key-major in LDS; the V^T
+// operand of the PV product is read with ds_read_b64_tr_b16, which, within each 16-lane
+// group, hands lane i element j of the 4x4 blocks supplied by lanes 4j + i/4 -- so lanes
+// pointing at V[k0 + s/4][d0 + 4(s%4)] receive V[k0 + j][d0 + i], the keys-in-registers
+// layout the MFMA needs. Tiles are 64 rows x 256 bytes with XOR-swizzled 16-byte chunks:
+//   K: chunk c of row r at c ^ (r & 15)       (16 consecutive rows at one c: distinct banks)
+//   V: chunk c of row r at c ^ ((r & 3) << 1) (the 4 rows of one transposing read: distinct)
+// One direct load writes 1 KB (4 rows) of a tile; lane i fills physical chunk i%16 of row
+// i/16 and so fetches the logical chunk that the swizzle puts there. Each key segment (cache
+// slots, then the call's own K/V) is tiled on its own; rows past a segment's end are read
+// as zeros through the buffer resource's range check and masked.
+// ---------------------------------------------------------------------------------------
+constexpr int DT_ROW = 256;                 // bytes per key row (128 bf16)
+constexpr int DT_TILE = BN * DT_ROW;        // 16 KB per K or V tile
+constexpr int DT_BUF = 2 * DT_TILE;         // K then V
+constexpr int DT_LDS = 2 * DT_BUF;          // double-buffered
+
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_direct_kernel(Params p) {
+  constexpr int D = 128;
+  constexpr int IPW = DT_TILE / 1024 / NW;  // direct loads per wave per tensor per tile
+  static_assert(IPW * NW * 1024 == DT_TILE, "tile must split evenly over the waves");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int G = p.n_wg;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int qd = G >> 3, rm = G & 7;
+  const int tile_id = (xcd < rm ? xcd * (qd + 1) : rm * (qd + 1) + (xcd - rm) * qd) + idx;
+  const int h = tile_id / p.n_qblk;
+  const int qblk = p.n_qblk - 1 - (tile_id % p.n_qblk);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int row0 = qblk * (NW * 32);
+  const int row = row0 + wave * 32 + l32;
+  const int lim = row_limit(p, row < p.nq ? row : p.nq - 1);
+  const int wave_min_lim = row_limit(p, min(row0 + wave * 32, p.nq - 1));
+  const int kend = row_limit(p, min(row0 + NW * 32 - 1, p.nq - 1));
+  // tiles per segment; in block-causal mode only segment A holds keys and the last visible
+  // key of the block bounds the loop
+  const int na = p.a.n;
+  const int ntA = ((p.vis_mode == 0 ? na : min(na, kend)) + BN - 1) / BN;
+  const int ntB = p.vis_mode == 0 ? (p.b.n + BN - 1) / BN : 0;
+  const int ntiles = ntA + ntB;
+
+  bf16x8_t qreg[D / 16];
+  {
+    const uint16_t* qp = p.q + int64_t(row < p.nq ? row : 0) * p.q_row + h * D + 8 * hi;
+#pragma unroll
+    for (int ss = 0; ss < D / 16; ++ss) {
+      const uint4 x = row < p.nq ? *reinterpret_cast<const uint4*>(qp + 16 * ss) : make_uint4(0, 0, 0, 0);
+      qreg[ss] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16_t{};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+
+  // LDS read lane bases. K (A operand of S^T = K Q^T): row kb*32 + l32, logical chunk
+  // 2ss + hi -> one base per ss. V (A operand of O^T = V^T P^T, via the transposing read):
+  // lane s of a 16-lane group points at row k0 + s/4, column db*32 + 16g + 4(s%4); the
+  // swizzle couples db's parity, so two bases.
+  int kbase[D / 16];
+#pragma unroll
+  for (int ss = 0; ss < D / 16; ++ss) kbase[ss] = l32 * DT_ROW + (((2 * ss + hi) ^ (l32 & 15)) << 4);
+  int vbase[2];
+  {
+    const int sl = lane & 15, g1 = (lane >> 4) & 1;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int c = 4 * par + 2 * g1 + ((sl >> 1) & 1);
+      vbase[par] = (4 * hi + (sl >> 2)) * DT_ROW + ((c ^ ((sl >> 2) << 1)) << 4) + 8 * (sl & 1);
+    }
+  }
+
+  // direct-load lane offsets inside a tile: instruction n of this wave fills rows
+  // (wave*IPW + n)*4 + lane/16, physical chunk lane%16
+  int lrow[IPW], ck[IPW], cv[IPW];
+#pragma unroll
+  for (int n = 0; n < IPW; ++n) {
+    lrow[n] = (wave * IPW + n) * 4 + (lane >> 4);
+    ck[n] = (lane & 15) ^ (lrow[n] & 15);
+    cv[n] = (lane & 15) ^ ((lrow[n] & 3) << 1);
+  }
+
+  // zero both buffers once, so rows that a range-checked load skips never hold non-finite bits
+  for (int i = tid; i < DT_LDS / 16; i += NW * 64) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  auto issue = [&](int t, uint8_t* buf) {
+    const bool inA = t < ntA;
+    const DevSeg& sg = inA ? p.a : p.b;
+    const int r0 = (inA ? t : t - ntA) * BN;                  // first row of the tile in the segment
+    const int64_t rp = sg.row_stride * 2;                      // row pitch in bytes
+    const uint8_t* kb0 = sg.k + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
+    const uint8_t* vb0 = sg.v + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
+    const int left = sg.n - r0;                                // rows of this segment from r0 on
+    const uint32_t bytes = left > 0 ? uint32_t(left - 1) * uint32_t(rp) + DT_ROW : 0u;
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kb0, bytes), rv = rsrc(vb0, bytes);
+#pragma unroll
+    for (int n = 0; n < IPW; ++n) {
+      const uint32_t ro = uint32_t(lrow[n]) * uint32_t(rp);
+      lds_load16(rk, buf + (wave * IPW + n) * 1024, ro + (ck[n] << 4));
+      lds_load16(rv, buf + DT_TILE + (wave * IPW + n) * 1024, ro + (cv[n] << 4));
+    }
+  };
+
+  issue(0, smem);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) issue(t + 1, smem + ((t + 1) & 1) * DT_BUF);
+    const uint8_t* kt = smem + (t & 1) * DT_BUF;
+    const uint8_t* vt = kt + DT_TILE;
+
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16_t{};
+#pragma unroll
+      for (int ss = 0; ss < D / 16; ++ss) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kbase[ss] + kb * 32 * DT_ROW);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ss], s[kb], 0, 0, 0);
+      }
+    }
+
+    // mask: rows past the segment's end, and keys past this row's block-causal limit
+    const bool inA = t < ntA;
+    const int r0 = (inA ? t : t - ntA) * BN;
+    const int seg_left = (inA ? na : p.b.n) - r0;
+    const int key0 = (inA ? 0 : na) + r0;                      // key index of the tile's row 0
+    if (seg_left < BN || key0 + BN > wave_min_lim) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (kr >= seg_left || key0 + kr >= lim) s[kb][r] = -__builtin_inff();
+        }
+    }
+
+    bf16x8_t pb[2][2];
+    softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
+
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint8_t* a0 = vt + vbase[db & 1] + (db >> 1) * 128 + (kb * 32 + 16 * j) * DT_ROW;
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(a0));
+          const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(a0 + 8 * DT_ROW));
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][j], oacc[db], 0, 0, 0);
+        }
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of tile t+1 have landed
+    __syncthreads();
+  }
+
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                     false, false);
+    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (row < p.nq) {
+    const float inv = 1.0f / l_run;
+    uint16_t* op = p.o + int64_t(row) * p.q_row + h * D + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 u;
+        u.x = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+        u.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(op + db * 32 + 8 * g) = u;
+      }
+  }
+}
+
+template <int NW>
+int launch_direct(const Params& p, int grid, hipStream_t stream, char* err) {
+  auto kern = attn_bf16_direct_kernel<NW>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, DT_LDS) != hipSuccess) {
+      snprintf(err, 256, "cannot set %d bytes of LDS", DT_LDS);
+      return 1;
+    }
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), DT_LDS, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(err, 256, "%s", hipGetErrorString(e));
+    return 1;
+  }
+  return 0;
 }
 
 template <int D, int NW, bool FP4>
@@ -517,7 +740,8 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp4 = p.a.fp4 != 0;
   if (a.D == 128) {
-    return fp4 ? launch_t<128, NW, true>(p, p.n_wg, s, err) : launch_t<128, NW, false>(p, p.n_wg, s, err);
+    // dense keys: direct-to-LDS staging; FP4 keys: register staging with fused dequant
+    return fp4 ? launch_t<128, NW, true>(p, p.n_wg, s, err) : launch_direct<NW>(p, p.n_wg, s, err);
   }
   if (a.D == 64) {
     return fp4 ? launch_t<64, NW, true>(p, p.n_wg, s, err) : launch_t<64, NW, false>(p, p.n_wg, s, err);
