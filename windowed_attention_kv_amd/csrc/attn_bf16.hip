@@ -469,19 +469,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // as zeros through the buffer resource's range check and masked.
 // ---------------------------------------------------------------------------------------
 constexpr int DT_ROW = 256;                 // bytes per key row (128 bf16)
-constexpr int DT_TILE = BN * DT_ROW;        // 16 KB per K or V tile
-constexpr int DT_BUF = 2 * DT_TILE;         // K then V
-constexpr int DT_LDS = 2 * DT_BUF;          // double-buffered
+
+// LDS plan of the direct kernel: SUB 64-key sub-tiles per barrier, K then V, double-buffered
+template <int SUB>
+struct DtCfg {
+  static constexpr int ROWS = BN * SUB;
+  static constexpr int TILE = ROWS * DT_ROW;   // one K or V tile
+  static constexpr int BUF = 2 * TILE;
+  static constexpr int LDS = 2 * BUF;
+};
 
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
                                            voff, 0, 0, 0);
 }
 
-template <int NW>
+template <int NW, int SUB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_direct_kernel(Params p) {
   constexpr int D = 128;
+  using T = DtCfg<SUB>;
+  constexpr int DT_TILE = T::TILE, DT_BUF = T::BUF, DT_LDS = T::LDS, TR = T::ROWS;
   constexpr int IPW = DT_TILE / 1024 / NW;  // direct loads per wave per tensor per tile
   static_assert(IPW * NW * 1024 == DT_TILE, "tile must split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -505,8 +513,8 @@ void attn_bf16_direct_kernel(Params p) {
   // tiles per segment; in block-causal mode only segment A holds keys and the last visible
   // key of the block bounds the loop
   const int na = p.a.n;
-  const int ntA = ((p.vis_mode == 0 ? na : min(na, kend)) + BN - 1) / BN;
-  const int ntB = p.vis_mode == 0 ? (p.b.n + BN - 1) / BN : 0;
+  const int ntA = ((p.vis_mode == 0 ? na : min(na, kend)) + TR - 1) / TR;
+  const int ntB = p.vis_mode == 0 ? (p.b.n + TR - 1) / TR : 0;
   const int ntiles = ntA + ntB;
 
   bf16x8_t qreg[D / 16];
@@ -558,7 +566,7 @@ void attn_bf16_direct_kernel(Params p) {
   auto issue = [&](int t, uint8_t* buf) {
     const bool inA = t < ntA;
     const DevSeg& sg = inA ? p.a : p.b;
-    const int r0 = (inA ? t : t - ntA) * BN;                  // first row of the tile in the segment
+    const int r0 = (inA ? t : t - ntA) * TR;                  // first row of the tile in the segment
     const int64_t rp = sg.row_stride * 2;                      // row pitch in bytes
     const uint8_t* kb0 = sg.k + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
     const uint8_t* vb0 = sg.v + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
@@ -579,7 +587,9 @@ void attn_bf16_direct_kernel(Params p) {
 
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) issue(t + 1, smem + ((t + 1) & 1) * DT_BUF);
-    const uint8_t* kt = smem + (t & 1) * DT_BUF;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+    const uint8_t* kt = smem + (t & 1) * DT_BUF + u * BN * DT_ROW;
     const uint8_t* vt = kt + DT_TILE;
 
     f32x16_t s[2];
@@ -595,9 +605,10 @@ void attn_bf16_direct_kernel(Params p) {
 
     // mask: rows past the segment's end, and keys past this row's block-causal limit
     const bool inA = t < ntA;
-    const int r0 = (inA ? t : t - ntA) * BN;
+    const int r0 = (inA ? t : t - ntA) * TR + u * BN;
     const int seg_left = (inA ? na : p.b.n) - r0;
-    const int key0 = (inA ? 0 : na) + r0;                      // key index of the tile's row 0
+    const int key0 = (inA ? 0 : na) + r0;                      // key index of the sub-tile's row 0
+    if (seg_left <= 0) continue;                               // a sub-tile wholly past the end
     if (seg_left < BN || key0 + BN > wave_min_lim) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -627,6 +638,7 @@ void attn_bf16_direct_kernel(Params p) {
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][j], oacc[db], 0, 0, 0);
         }
     }
+    }
 
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of tile t+1 have landed
     __syncthreads();
@@ -652,9 +664,10 @@ void attn_bf16_direct_kernel(Params p) {
   }
 }
 
-template <int NW>
+template <int NW, int SUB>
 int launch_direct(const Params& p, int grid, hipStream_t stream, char* err) {
-  auto kern = attn_bf16_direct_kernel<NW>;
+  auto kern = attn_bf16_direct_kernel<NW, SUB>;
+  constexpr int DT_LDS = DtCfg<SUB>::LDS;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -741,7 +754,12 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
   const bool fp4 = p.a.fp4 != 0;
   if (a.D == 128) {
     // dense keys: direct-to-LDS staging; FP4 keys: register staging with fused dequant
-    return fp4 ? launch_t<128, NW, true>(p, p.n_wg, s, err) : launch_direct<NW>(p, p.n_wg, s, err);
+    if (fp4) return launch_t<128, NW, true>(p, p.n_wg, s, err);
+    // 8 waves x 32 rows per workgroup, 128 keys per barrier, 2 workgroup waves per SIMD
+    constexpr int DNW = 8, DSUB = 2;
+    p.n_qblk = (a.nq + DNW * 32 - 1) / (DNW * 32);
+    p.n_wg = p.n_qblk * a.H;
+    return launch_direct<DNW, DSUB>(p, p.n_wg, s, err);
   }
   if (a.D == 64) {
     return fp4 ? launch_t<64, NW, true>(p, p.n_wg, s, err) : launch_t<64, NW, false>(p, p.n_wg, s, err);
