@@ -462,7 +462,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // pointing at V[k0 + s/4][d0 + 4(s%4)] receive V[k0 + j][d0 + i], the keys-in-registers
 // layout the MFMA needs. Tiles are 64 rows x 256 bytes with XOR-swizzled 16-byte chunks:
 //   K: chunk c of row r at c ^ (r & 15)       (16 consecutive rows at one c: distinct banks)
-//   V: chunk c of row r at c ^ ((r & 3) << 1) (the 4 rows of one transposing read: distinct)
+//   V: chunk c of row r at c ^ ((r & 3) << 2) (the 4 rows x 2 lane groups of one
+//      transposing read land on 16 distinct chunks)
 // One direct load writes 1 KB (4 rows) of a tile; lane i fills physical chunk i%16 of row
 // i/16 and so fetches the logical chunk that the swizzle puts there. Each key segment (cache
 // slots, then the call's own K/V) is tiled on its own; rows past a segment's end are read
@@ -484,7 +485,7 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* ld
                                            voff, 0, 0, 0);
 }
 
-template <int NW, int SUB>
+template <int NW, int SUB, bool PRIO>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_direct_kernel(Params p) {
   constexpr int D = 128;
@@ -535,17 +536,17 @@ void attn_bf16_direct_kernel(Params p) {
   // LDS read lane bases. K (A operand of S^T = K Q^T): row kb*32 + l32, logical chunk
   // 2ss + hi -> one base per ss. V (A operand of O^T = V^T P^T, via the transposing read):
   // lane s of a 16-lane group points at row k0 + s/4, column db*32 + 16g + 4(s%4); the
-  // swizzle couples db's parity, so two bases.
+  // swizzle XORs db's two bits, so four bases.
   int kbase[D / 16];
 #pragma unroll
   for (int ss = 0; ss < D / 16; ++ss) kbase[ss] = l32 * DT_ROW + (((2 * ss + hi) ^ (l32 & 15)) << 4);
-  int vbase[2];
+  int vbase[4];
   {
     const int sl = lane & 15, g1 = (lane >> 4) & 1;
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int c = 4 * par + 2 * g1 + ((sl >> 1) & 1);
-      vbase[par] = (4 * hi + (sl >> 2)) * DT_ROW + ((c ^ ((sl >> 2) << 1)) << 4) + 8 * (sl & 1);
+    for (int db = 0; db < 4; ++db) {
+      const int c = 4 * db + 2 * g1 + ((sl >> 1) & 1);
+      vbase[db] = (4 * hi + (sl >> 2)) * DT_ROW + ((c ^ ((sl >> 2) << 2)) << 4) + 8 * (sl & 1);
     }
   }
 
@@ -556,7 +557,7 @@ void attn_bf16_direct_kernel(Params p) {
   for (int n = 0; n < IPW; ++n) {
     lrow[n] = (wave * IPW + n) * 4 + (lane >> 4);
     ck[n] = (lane & 15) ^ (lrow[n] & 15);
-    cv[n] = (lane & 15) ^ ((lrow[n] & 3) << 1);
+    cv[n] = (lane & 15) ^ ((lrow[n] & 3) << 2);
   }
 
   // zero both buffers once, so rows that a range-checked load skips never hold non-finite bits
@@ -593,6 +594,7 @@ void attn_bf16_direct_kernel(Params p) {
     const uint8_t* vt = kt + DT_TILE;
 
     f32x16_t s[2];
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16_t{};
@@ -602,6 +604,7 @@ void attn_bf16_direct_kernel(Params p) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ss], s[kb], 0, 0, 0);
       }
     }
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
 
     // mask: rows past the segment's end, and keys past this row's block-causal limit
     const bool inA = t < ntA;
@@ -622,13 +625,14 @@ void attn_bf16_direct_kernel(Params p) {
     bf16x8_t pb[2][2];
     softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
 
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const uint8_t* a0 = vt + vbase[db & 1] + (db >> 1) * 128 + (kb * 32 + 16 * j) * DT_ROW;
+          const uint8_t* a0 = vt + vbase[db] + (kb * 32 + 16 * j) * DT_ROW;
           const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4i16_t*)(a0));
           const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -638,6 +642,7 @@ void attn_bf16_direct_kernel(Params p) {
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][j], oacc[db], 0, 0, 0);
         }
     }
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of tile t+1 have landed
@@ -664,9 +669,9 @@ void attn_bf16_direct_kernel(Params p) {
   }
 }
 
-template <int NW, int SUB>
+template <int NW, int SUB, bool PRIO>
 int launch_direct(const Params& p, int grid, hipStream_t stream, char* err) {
-  auto kern = attn_bf16_direct_kernel<NW, SUB>;
+  auto kern = attn_bf16_direct_kernel<NW, SUB, PRIO>;
   constexpr int DT_LDS = DtCfg<SUB>::LDS;
   static bool attr_set = false;
   if (!attr_set) {
@@ -759,7 +764,9 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
     constexpr int DNW = 8, DSUB = 2;
     p.n_qblk = (a.nq + DNW * 32 - 1) / (DNW * 32);
     p.n_wg = p.n_qblk * a.H;
-    return launch_direct<DNW, DSUB>(p, p.n_wg, s, err);
+    static const bool noprio = getenv("LL_ATTN_NOPRIO") != nullptr;  // tuning experiment
+    return noprio ? launch_direct<DNW, DSUB, false>(p, p.n_wg, s, err)
+                  : launch_direct<DNW, DSUB, true>(p, p.n_wg, s, err);
   }
   if (a.D == 64) {
     return fp4 ? launch_t<64, NW, true>(p, p.n_wg, s, err) : launch_t<64, NW, false>(p, p.n_wg, s, err);
