@@ -485,7 +485,7 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* ld
                                            voff, 0, 0, 0);
 }
 
-template <int NW, int SUB, bool PRIO>
+template <int NW, int SUB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_direct_kernel(Params p) {
   constexpr int D = 128;
@@ -594,7 +594,6 @@ void attn_bf16_direct_kernel(Params p) {
     const uint8_t* vt = kt + DT_TILE;
 
     f32x16_t s[2];
-    if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16_t{};
@@ -604,7 +603,6 @@ void attn_bf16_direct_kernel(Params p) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ss], s[kb], 0, 0, 0);
       }
     }
-    if (PRIO) __builtin_amdgcn_s_setprio(0);
 
     // mask: rows past the segment's end, and keys past this row's block-causal limit
     const bool inA = t < ntA;
@@ -625,7 +623,6 @@ void attn_bf16_direct_kernel(Params p) {
     bf16x8_t pb[2][2];
     softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
 
-    if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -642,7 +639,6 @@ void attn_bf16_direct_kernel(Params p) {
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][j], oacc[db], 0, 0, 0);
         }
     }
-    if (PRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of tile t+1 have landed
@@ -669,9 +665,9 @@ void attn_bf16_direct_kernel(Params p) {
   }
 }
 
-template <int NW, int SUB, bool PRIO>
+template <int NW, int SUB>
 int launch_direct(const Params& p, int grid, hipStream_t stream, char* err) {
-  auto kern = attn_bf16_direct_kernel<NW, SUB, PRIO>;
+  auto kern = attn_bf16_direct_kernel<NW, SUB>;
   constexpr int DT_LDS = DtCfg<SUB>::LDS;
   static bool attr_set = false;
   if (!attr_set) {
@@ -764,9 +760,7 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
     constexpr int DNW = 8, DSUB = 2;
     p.n_qblk = (a.nq + DNW * 32 - 1) / (DNW * 32);
     p.n_wg = p.n_qblk * a.H;
-    static const bool noprio = getenv("LL_ATTN_NOPRIO") != nullptr;  // tuning experiment
-    return noprio ? launch_direct<DNW, DSUB, false>(p, p.n_wg, s, err)
-                  : launch_direct<DNW, DSUB, true>(p, p.n_wg, s, err);
+    return launch_direct<DNW, DSUB>(p, p.n_wg, s, err);
   }
   if (a.D == 64) {
     return fp4 ? launch_t<64, NW, true>(p, p.n_wg, s, err) : launch_t<64, NW, false>(p, p.n_wg, s, err);
