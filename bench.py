@@ -50,6 +50,27 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
 
 
+def counter_traffic(avg_flops_per_launch):
+    """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE summary, but only
+    while the kernel source is the one the counters were taken on (else None)."""
+    import hashlib
+    src = os.path.join(ROOT, "windowed_attention_kv_amd", "csrc", "attn_bf16.hip")
+    prof = os.path.join(ROOT, "profiles", "attn_commit_traffic_counters.md")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        kv = {}
+        for line in open(prof):
+            if ":" in line and line.startswith("    "):
+                k, v = line.strip().split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("source_sha256_prefix") != sha:
+            return None
+        return round((float(kv["fetch_kib_per_launch"]) * float(kv["read_scale"])
+                      + float(kv["write_kib_per_launch"]) * float(kv["write_scale"])) * 1024)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def visible_keys(chunk, C, S, W, T):
     s = chunk * C
     frames = set(range(min(S, s + C))) | set(range(max(0, s - W), s)) | set(range(s, s + C))
@@ -150,13 +171,77 @@ def cpu_baseline(shape):
                        f"{dt:.2f} s measured, scaled by flops to the 20-chunk stream")}
 
 
+def stack_row(torch, shape, Cache, attn_flops, kv_format, pool):
+    """The stack workload: L layers x 4 denoise steps x 80 chunks (only the last step of a
+    chunk commits), one pass from an empty cache. Inputs cycle through a pool of resident
+    synthetic sets (values do not change the work). Timed as a whole with events."""
+    L, steps, chunks = 30, 4, 80
+    n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
+    C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
+    cache = Cache(L, H, D, T, C, S, W, kv_format=kv_format)
+    out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+    flops = 0.0
+    for c in range(chunks):
+        flops += L * steps * attn_flops(n, visible_keys(c, C, S, W, T), H, D)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    i = 0
+    for c in range(chunks):
+        for st in range(steps):
+            for layer in range(L):
+                q, k, v = pool[i % len(pool)]
+                i += 1
+                cache.attn_chunk(layer, q, k, v, out=out)
+                if st == steps - 1:
+                    cache.commit(layer, k, v)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    rows = n * L * steps * chunks
+    return {"ms": round(ms, 2), "query_rows": rows, "query_tokens_per_s": round(rows / ms * 1e3, 1),
+            "tflops": round(flops / ms / 1e9, 1),
+            "frac_bf16_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "pflop": round(flops / 1e15, 4),
+            "work": f"{L} layers x {steps} steps x {chunks} chunks, {kv_format} KV, attention + commits"}
+
+
+def commit_batch_row(torch, shape, Cache, kv_format, k, v):
+    """Per-commit time of 30 back-to-back commits (one per layer of a 30-layer cache), the
+    pattern of the stack workload; events bracket each batch of 30."""
+    L = 30
+    n, H, D = shape.n_query, shape.heads, shape.head_dim
+    cache = Cache(L, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
+                  shape.window_frames, kv_format=kv_format)
+    for layer in range(L):
+        cache.commit(layer, k, v)
+    tm = EventTimer(torch)
+    for rep in range(10):
+        s = tm.start()
+        for layer in range(L):
+            cache.commit(layer, k, v)
+        tm.stop(s, "batch")
+    torch.cuda.synchronize()
+    ms = tm.totals()["batch"][0] / (10 * L)
+    if kv_format == "fp4":
+        nbytes = 2 * n * H * D * 2 + 2 * n * H * (D // 2 + D // 16)
+    else:
+        nbytes = 2 * 2 * n * H * D * 2
+    gbs = nbytes / ms / 1e6
+    return {"us_per_commit": round(ms * 1e3, 3), "bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
-    """FP4 stream, standalone quant and the recache, each timed with events."""
+    """Commit batches, FP4 stream, standalone quant, recache and the 30-layer stacks."""
     res = {}
     n, H, D = shape.n_query, shape.heads, shape.head_dim
     inputs = gen_inputs(torch, shape.chunks, n, H, D, 7, "cuda")
     out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
-    # FP4 KV store at the layer shape
+    res["commit_30_layers"] = commit_batch_row(torch, shape, Cache, "dense", inputs[0][1], inputs[0][2])
+    res["fp4_commit_30_layers"] = commit_batch_row(torch, shape, Cache, "fp4", inputs[0][1], inputs[0][2])
+    # FP4 KV store at the layer shape: steady-state attention (15 visible frames)
     c4 = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
                shape.window_frames, kv_format="fp4")
     for rep in range(3):
@@ -166,19 +251,28 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
             s = tm.start()
             c4.attn_chunk(0, q, k, v, out=out)
             tm.stop(s, "attn_steady" if c >= 4 else "attn_fill")
-            s = tm.start()
             c4.commit(0, k, v)
-            tm.stop(s, "commit")
         torch.cuda.synchronize()
     tot = tm.totals()
     steady_flops = attn_flops(n, 23400, H, D)
-    res["fp4_attention_steady"] = {
-        "ms": round(tot["attn_steady"][0] / tot["attn_steady"][1], 4),
-        "tflops": round(steady_flops / (tot["attn_steady"][0] / tot["attn_steady"][1]) / 1e9, 1)}
-    fp4_commit_bytes = n * H * D * 2 * 2 + 2 * n * H * (D // 2 + D // 16)
-    ms = tot["commit"][0] / tot["commit"][1]
-    res["fp4_commit"] = {"ms": round(ms, 5), "bytes": fp4_commit_bytes,
-                         "gbs": round(fp4_commit_bytes / ms / 1e6, 1)}
+    ms = tot["attn_steady"][0] / tot["attn_steady"][1]
+    res["fp4_attention_steady"] = {"ms": round(ms, 4), "tflops": round(steady_flops / ms / 1e9, 1),
+                                   "frac_bf16_peak": round(steady_flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    # dense steady-state attention for comparison
+    cd = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
+               shape.window_frames)
+    tm = EventTimer(torch)
+    for c, (q, k, v) in enumerate(inputs):
+        s = tm.start()
+        cd.attn_chunk(0, q, k, v, out=out)
+        tm.stop(s, "attn_steady" if c >= 4 else "attn_fill")
+        cd.commit(0, k, v)
+    torch.cuda.synchronize()
+    tot = tm.totals()
+    ms = tot["attn_steady"][0] / tot["attn_steady"][1]
+    res["attention_steady"] = {"ms": round(ms, 4), "tflops": round(steady_flops / ms / 1e9, 1),
+                               "frac_bf16_peak": round(steady_flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "keys": 23400}
     # standalone quant of one 12-frame cache (K and V): 2 x 18720 x 1536 elements
     x = torch.randn((2 * 18720 * H, D), device="cuda").mul_(0.5).to(torch.bfloat16)
     pk = torch.empty((x.shape[0], D // 2), dtype=torch.uint8, device="cuda")
@@ -193,13 +287,16 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     torch.cuda.synchronize()
     ms = tm.totals()["quant"][0] / 10
     qbytes = x.numel() * 2 + pk.numel() + sc.numel()
-    res["kv_quant_12_frames"] = {"ms": round(ms, 5), "bytes": qbytes,
-                                 "gbs": round(qbytes / ms / 1e6, 1)}
-    # recache of one layer at the prompt-switch shape (12 held frames, 512 text tokens)
-    cr = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
+    res["kv_quant_12_frames"] = {"ms": round(ms, 5), "bytes": qbytes, "gbs": round(qbytes / ms / 1e6, 1),
+                                 "frac_hbm": round(qbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del x, pk, sc
+    # recache at the prompt-switch shape (12 held frames, 512 text tokens), 30 layers
+    L = 30
+    cr = Cache(L, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
                shape.window_frames)
     for c in range(10):
-        cr.commit(0, inputs[c][1], inputs[c][2])
+        for layer in range(L):
+            cr.commit(layer, inputs[c][1], inputs[c][2])
     rows = 12 * shape.tokens_per_frame
     g = torch.Generator(device="cuda")
     g.manual_seed(11)
@@ -209,20 +306,27 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
            for _ in range(2)]
     o = torch.empty_like(big[0])
     ox = torch.empty_like(big[0])
-    for _ in range(2):
-        cr.recache(0, big[0], big[1], big[2], big[3], txt[0], txt[1], out=o, out_x=ox)
+    cr.recache(0, big[0], big[1], big[2], big[3], txt[0], txt[1], out=o, out_x=ox)
+    torch.cuda.synchronize()
     tm = EventTimer(torch)
-    for _ in range(5):
+    for _ in range(2):
         s = tm.start()
-        cr.recache(0, big[0], big[1], big[2], big[3], txt[0], txt[1], out=o, out_x=ox)
+        for layer in range(L):
+            cr.recache(layer, big[0], big[1], big[2], big[3], txt[0], txt[1], out=o, out_x=ox)
         tm.stop(s, "recache")
     torch.cuda.synchronize()
-    ms = tm.totals()["recache"][0] / 5
-    # visible pairs: group g of 4680 rows sees (g+1)*4680 keys
-    self_pairs = sum(4680 * (g + 1) * 4680 for g in range(4))
-    fl = (self_pairs + rows * 512) * H * 4 * D
-    res["recache_layer"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
-                            "note": "self block-causal + cross (512 text keys) + rewrite, one layer"}
+    ms = tm.totals()["recache"][0] / 2
+    # visible pairs: group g of 4680 rows sees (g+1)*4680 keys; cross: 512 keys
+    self_pairs = sum(4680 * (gg + 1) * 4680 for gg in range(4))
+    fl = L * (self_pairs + rows * 512) * H * 4 * D
+    res["recache_30_layers"] = {"ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
+                                "frac_bf16_peak": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                "query_tokens_per_s": round(L * rows / ms * 1e3, 1),
+                                "note": "per layer: block-causal self + cross (512 text keys) + slot rewrite"}
+    del cr, big, txt, o, ox
+    pool = gen_inputs(torch, 8, n, H, D, 21, "cuda")
+    res["stack_dense"] = stack_row(torch, shape, Cache, attn_flops, "dense", pool)
+    res["stack_fp4"] = stack_row(torch, shape, Cache, attn_flops, "fp4", pool)
     return res
 
 
@@ -289,8 +393,13 @@ def main():
                    "tflops_whole_step": round(flops_step / (ms_step / 1e3) / 1e12, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_bf16_kernel<128,4,false>",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": counter_traffic(attn_flops_launch),
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x read scale + WRITE_SIZE x write scale)",
+                     # Q and O (n x H x D bf16 each) + the visible keys' K and V: per launch the
+                     # K/V bytes are 2 * keys * H * D * 2 = flops_per_launch / n
+                     "algorithmic_bytes_per_launch": round(2 * n * H * D * 2 + attn_flops_launch / n),
+                     "kernel": "attn_bf16_direct_kernel<8,2>",
                      "avg_launch_ms": round(attn_ms, 4),
                      "avg_flops_per_launch": attn_flops_launch},
         "rows": {"commit": {"avg_launch_ms": round(commit_ms, 5), "bytes": commit_bytes,

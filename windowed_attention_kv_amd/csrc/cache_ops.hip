@@ -3,8 +3,8 @@
 //
 // Commit ("LongLive" summary page, 方法 §3 高效长推理): a chunk's K/V frames are written into
 // the layer's slots; a window slot is overwritten in place, which IS the eviction of the frame
-// W earlier, so eviction moves no bytes. One launch covers K and V (blockIdx.y), one
-// workgroup per token row, 16-byte coalesced loads and stores.
+// W earlier, so eviction moves no bytes. One launch covers K and V (blockIdx.y), with
+// 16-byte coalesced loads and stores over consecutive token rows.
 //
 // FP4 store ("LongLive 2.0" distributed-inference page, NVFP4 / KV cache section; element
 // and scale encodings of the OCP MX v1.0 E2M1 / E8M0 tables): per block of 16 bf16 values
@@ -58,7 +58,24 @@ __device__ __forceinline__ uint32_t quant16(uint4 a, uint4 b, uint2& packed) {
   return sb;
 }
 
+// Quantise 64 consecutive bf16 values (four 16-element blocks) at `src`: 32 packed bytes
+// and the 4 scale bytes (block i in byte i).
+__device__ __forceinline__ void quant64(const uint8_t* src, uint4& pk0, uint4& pk1, uint32_t& sc) {
+  uint4 x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = reinterpret_cast<const uint4*>(src)[i];
+  uint2 p[4];
+  sc = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) sc |= quant16(x[2 * b], x[2 * b + 1], p[b]) << (8 * b);
+  pk0 = make_uint4(p[0].x, p[0].y, p[1].x, p[1].y);
+  pk1 = make_uint4(p[2].x, p[2].y, p[3].x, p[3].y);
+}
+
 struct ScatterP {
+  int32_t row0;              // first token row of this launch (launches are split below 2^24 units)
+  int32_t ring0;             // (frame - S) mod W of the first non-lead frame
+  float inv_w;               // 1 / W
   const uint8_t* src[2];
   uint8_t* dst[2];
   uint8_t* dst_scales[2];
@@ -67,51 +84,77 @@ struct ScatterP {
   int64_t first_ring;
 };
 
-__device__ __forceinline__ int32_t slot_of_rank(const ScatterP& p, int32_t r) {
-  if (r < p.n_lead) return p.lead_slot0 + r;
-  return p.S + int32_t((p.first_ring + (r - p.n_lead)) % p.W);
+// i / d for 0 <= i < 2^24 and 0 < d < 2^16, via a float reciprocal and one correction step
+// (the float estimate is off by at most one).
+__device__ __forceinline__ int32_t fdiv(int32_t i, int32_t d, float inv) {
+  int32_t q = int32_t(float(i) * inv);
+  const int32_t r = i - q * d;
+  q += (r < 0) ? -1 : (r >= d ? 1 : 0);
+  return q;
 }
 
-// dense: one workgroup per (token row, K|V); units of 16 bytes
-__global__ __launch_bounds__(256) void scatter_dense_kernel(ScatterP p) {
-  const int32_t tr = blockIdx.x;
+// Slot of source frame rank r: lead (sink) frames first, then the window ring.
+__device__ __forceinline__ int32_t slot_of_rank(const ScatterP& p, int32_t r) {
+  if (r < p.n_lead) return p.lead_slot0 + r;
+  const int32_t k = p.ring0 + (r - p.n_lead);
+  return p.S + (k - p.W * fdiv(k, p.W, p.inv_w));
+}
+
+// dense: one workgroup per (token row, K|V), 16-byte units; the row's slot is computed once
+__global__ __launch_bounds__(256) void scatter_dense_kernel(ScatterP p, int32_t n_units, int32_t units,
+                                                            float inv_units, float inv_t, int32_t uph_log2) {
+  const int32_t tr = p.row0 + blockIdx.x;
   const int which = blockIdx.y;
   const int32_t r = tr / p.T, t = tr - r * p.T;
   const int32_t slot = slot_of_rank(p, r);
-  const int32_t row_bytes = p.D * p.es;            // one head's row
-  const int32_t uph = row_bytes >> 4;              // 16-byte units per head row
-  const int32_t units = p.H * uph;
-  const uint8_t* src = p.src[which] + int64_t(tr) * p.H * row_bytes;
-  uint8_t* dst = p.dst[which];
+  const int32_t row_bytes = p.D * p.es;
+  const int32_t uph = row_bytes >> 4;
+  const uint8_t* src = p.src[which] + int64_t(tr) * units * 16;
   const int64_t head_plane = int64_t(p.slots) * p.T * row_bytes;
   const int64_t dst_row = (int64_t(slot) * p.T + t) * row_bytes;
   for (int32_t u = threadIdx.x; u < units; u += blockDim.x) {
-    const int32_t h = u / uph, c = u - h * uph;
+    const int32_t h = u >> uph_log2, cc = u & (uph - 1);
     const uint4 x = *reinterpret_cast<const uint4*>(src + int64_t(u) * 16);
-    *reinterpret_cast<uint4*>(dst + h * head_plane + dst_row + c * 16) = x;
+    *reinterpret_cast<uint4*>(p.dst[which] + h * head_plane + dst_row + cc * 16) = x;
   }
 }
 
-// fp4: one thread per 16-element block; one workgroup per (token row, K|V)
-__global__ __launch_bounds__(256) void scatter_fp4_kernel(ScatterP p) {
-  const int32_t tr = blockIdx.x;
+// fp4: one thread per 64 elements (4 scale blocks) of a (token, head) row, one workgroup per
+// 8 token rows and K|V: 32 packed bytes and one 4-byte scale word per thread. D % 64 == 0.
+__global__ __launch_bounds__(256) void scatter_fp4_kernel(ScatterP p, int32_t n_units, int32_t units,
+                                                          float inv_units, float inv_t, int32_t gph_log2) {
   const int which = blockIdx.y;
-  const int32_t r = tr / p.T, t = tr - r * p.T;
-  const int32_t slot = slot_of_rank(p, r);
-  const int32_t bph = p.D / 16;                    // blocks per head row
-  const int32_t nblk = p.H * bph;
-  const uint8_t* src = p.src[which] + int64_t(tr) * p.H * p.D * 2;
   const int64_t head_rows = int64_t(p.slots) * p.T;
-  const int64_t drow = int64_t(slot) * p.T + t;
-  for (int32_t b = threadIdx.x; b < nblk; b += blockDim.x) {
-    const int32_t h = b / bph, c = b - h * bph;
-    const uint4 x0 = *reinterpret_cast<const uint4*>(src + int64_t(b) * 32);
-    const uint4 x1 = *reinterpret_cast<const uint4*>(src + int64_t(b) * 32 + 16);
-    uint2 pk;
-    const uint32_t sb = quant16(x0, x1, pk);
-    const int64_t row = h * head_rows + drow;
-    *reinterpret_cast<uint2*>(p.dst[which] + row * (p.D / 2) + c * 8) = pk;
-    p.dst_scales[which][row * bph + c] = uint8_t(sb);
+  const int32_t tr0 = p.row0 + blockIdx.x * 8;
+  const int32_t nrows = n_units / units;
+  const int32_t nr = min(8, p.row0 + nrows - tr0);
+  for (int32_t i = threadIdx.x; i < nr * units; i += blockDim.x) {
+    const int32_t rl = i / units, g = i - rl * units;
+    const int32_t tr = tr0 + rl;
+    const int32_t r = tr / p.T, t = tr - r * p.T;
+    const int32_t h = g >> gph_log2, cc = g & ((1 << gph_log2) - 1);
+    uint4 pk0, pk1;
+    uint32_t sc;
+    quant64(p.src[which] + (int64_t(tr) * units + g) * 128, pk0, pk1, sc);
+    const int64_t row = h * head_rows + int64_t(slot_of_rank(p, r)) * p.T + t;
+    uint8_t* dp = p.dst[which] + row * (p.D / 2) + cc * 32;
+    reinterpret_cast<uint4*>(dp)[0] = pk0;
+    reinterpret_cast<uint4*>(dp)[1] = pk1;
+    *reinterpret_cast<uint32_t*>(p.dst_scales[which] + row * (p.D / 16) + cc * 4) = sc;
+  }
+}
+
+// standalone codec: one thread per 64 elements when the row length allows, else per 16
+__global__ __launch_bounds__(256) void quant64_kernel(const uint8_t* x, int64_t ngrp, uint8_t* packed,
+                                                      uint8_t* scales) {
+  for (int64_t g = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; g < ngrp;
+       g += int64_t(gridDim.x) * blockDim.x) {
+    uint4 pk0, pk1;
+    uint32_t sc;
+    quant64(x + g * 128, pk0, pk1, sc);
+    reinterpret_cast<uint4*>(packed + g * 32)[0] = pk0;
+    reinterpret_cast<uint4*>(packed + g * 32)[1] = pk1;
+    *reinterpret_cast<uint32_t*>(scales + g * 4) = sc;
   }
 }
 
@@ -194,12 +237,31 @@ int launch_scatter(const ScatterArgs& a, void* stream, char* err) {
   p.W = a.W;
   p.slots = a.slots;
   p.first_ring = a.first_ring;
-  const dim3 grid(a.n_frames * a.T, 2);
+  p.ring0 = int32_t(a.first_ring % a.W);
+  p.inv_w = 1.0f / float(a.W);
+  const int32_t n_rows = a.n_frames * a.T;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.fp4) {
-    hipLaunchKernelGGL(scatter_fp4_kernel, grid, dim3(block_for(a.H * a.D / 16)), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(scatter_dense_kernel, grid, dim3(block_for(a.H * a.D * p.es / 16)), 0, s, p);
+  const float inv_t = 1.0f / float(a.T);
+  if (a.fp4 && a.D % 64) {
+    snprintf(err, 256, "the FP4 store needs head_dim %% 64 == 0");
+    return 1;
+  }
+  const int32_t gph = a.D / 64;
+  const int32_t uph = a.D * p.es / 16;             // 8, 16 or 32
+  const int32_t units = a.fp4 ? a.H * gph : a.H * uph;
+  const int32_t rows_per_launch = ((1 << 24) - 1) / units;
+  for (int32_t r0 = 0; r0 < n_rows; r0 += rows_per_launch) {
+    p.row0 = r0;
+    const int32_t n_units = min(rows_per_launch, n_rows - r0) * units;
+    if (a.fp4) {
+      const int blocks = (n_units / units + 7) / 8;
+      hipLaunchKernelGGL(scatter_fp4_kernel, dim3(blocks, 2), dim3(256), 0, s, p, n_units, units,
+                         1.0f / float(units), inv_t, gph == 2 ? 1 : 0);
+    } else {
+      const int blocks = n_units / units;
+      hipLaunchKernelGGL(scatter_dense_kernel, dim3(blocks, 2), dim3(block_for(units)), 0, s, p, n_units, units,
+                         1.0f / float(units), inv_t, uph == 8 ? 3 : (uph == 16 ? 4 : 5));
+    }
   }
   return finish(err);
 }
@@ -207,10 +269,19 @@ int launch_scatter(const ScatterArgs& a, void* stream, char* err) {
 int launch_quant(const QuantArgs& a, void* stream, char* err) {
   const int64_t nblk = a.rows * a.row_len / 16;
   if (nblk == 0) return 0;
-  int64_t grid = (nblk + 255) / 256;
-  if (grid > 65536) grid = 65536;
-  hipLaunchKernelGGL(quant_kernel, dim3(unsigned(grid)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint8_t*>(a.x), nblk, a.packed, a.scales);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.row_len % 64 == 0) {
+    const int64_t ngrp = nblk / 4;
+    int64_t grid = (ngrp + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    hipLaunchKernelGGL(quant64_kernel, dim3(unsigned(grid)), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(a.x), ngrp, a.packed, a.scales);
+  } else {
+    int64_t grid = (nblk + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    hipLaunchKernelGGL(quant_kernel, dim3(unsigned(grid)), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(a.x), nblk, a.packed, a.scales);
+  }
   return finish(err);
 }
 
