@@ -77,8 +77,15 @@ typedef struct {
 
 typedef struct ll_cache ll_cache; /* opaque host handle */
 
-/* Bytes of device memory a cache with this descriptor needs (S+W frame slots per layer for K
- * and V, dense or FP4 planes). Fails with LL_EINVAL / LL_EUNSUPPORTED on a bad descriptor. */
+/* Bytes of device memory a cache with this descriptor needs: S+W frame slots per layer for K
+ * and V (dense or FP4 planes), and, for a dense bf16 head_dim-128 cache, a workspace after
+ * the last layer for the split schedule of ll_attn_chunk (used when a call has fewer
+ * (head, 256-row query block) pairs than the device has compute units, e.g. a few heads per
+ * GPU): one 32-bit counter per (head, query block), padded to 256 bytes, then
+ * 2 * min(CUs, blocks * tiles) slots of 135,168 bytes, with tiles = ceil((S+W)*T/128) +
+ * ceil(C*T/128). The CU count is that of the device current at the call, so create the
+ * cache with the same device current. Fails with LL_EINVAL / LL_EUNSUPPORTED on a bad
+ * descriptor. */
 ll_status ll_cache_size(const ll_cache_desc* desc, size_t* device_bytes);
 
 /* Create a handle over caller-owned device memory `device_mem` (256-byte aligned, at least
@@ -98,7 +105,9 @@ ll_status ll_cache_reset(ll_cache* cache);
  *   frames plus the last W committed frames; a frame counts once) followed by the chunk's
  *   own k, v (attended bidirectionally, never quantised).
  * May be called any number of times before the chunk is committed (one call per denoise
- * step); the cache is not modified. Pointers 16-byte aligned. */
+ * step); the cache's frames are not modified. Pointers 16-byte aligned. The first call on a
+ * handle also clears the split-schedule counters (a kernel on `stream`); calls share the
+ * workspace, so calls on one handle must not overlap on different streams. */
 ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const void* k,
                         const void* v, void* o, void* stream);
 

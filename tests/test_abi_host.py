@@ -60,7 +60,7 @@ P = ctypes.c_void_p(1 << 24)  # aligned dummy device pointer
 
 def _records(f):
     out = []
-    buf = (ctypes.c_int64 * 16)()
+    buf = (ctypes.c_int64 * 20)()
     for i in range(f.llfake_count()):
         kind = f.llfake_record(i, buf)
         out.append((kind, list(buf)))
@@ -200,20 +200,74 @@ def test_descriptor_validation(fake):
                                 ctypes.byref(h)) == _lib.LL_EINVAL
 
 
+def _split_workspace(H, n, cache_keys, n_cu):
+    """Workspace of the split attention schedule (dense bf16, head_dim 128): one 32-bit
+    counter per (head, 256-row query block), padded to 256 bytes, then two slots of
+    66 floats x 512 threads per workgroup of the largest launch (one per CU, at most one per
+    128-key unit)."""
+    blocks = H * -(-n // 256)
+    units = blocks * (-(-cache_keys // 128) + -(-n // 128))
+    g = min(n_cu, units)
+    return -(-blocks * 4 // 256) * 256 + 2 * g * 66 * 512 * 4
+
+
 def test_cache_bytes():
     """Cache size depends only on S+W (and the shape), per layer: 12 frames of 1560 tokens x
-    12 heads x 128 in bf16, K and V = 115.0 MB; FP4: 4.5 bits per element."""
+    12 heads x 128 in bf16, K and V = 115.0 MB, plus the split-schedule workspace (the
+    recording backend reports 256 CUs); FP4: 4.5 bits per element, no workspace."""
     if not os.path.exists(_lib.FAKE_PATH):
         pytest.skip("libll_fake.so not built")
     f = _lib.load_fake()
     size = ctypes.c_size_t()
     d = make_desc(1, 12, 128, 1560, 3, 3, 9)
     assert f.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == 0
-    assert size.value == 2 * 12 * 1560 * 12 * 128 * 2
+    assert size.value == 2 * 12 * 1560 * 12 * 128 * 2 + _split_workspace(12, 4680, 12 * 1560, 256)
     d = make_desc(30, 12, 128, 1560, 3, 3, 9, kv_format="fp4")
     assert f.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == 0
     elems = 12 * 1560 * 12 * 128
     assert size.value == 30 * 2 * (elems // 2 + elems // 16)
+
+
+def test_split_workspace_is_cleared_once_and_passed_to_chunk_attention(fake):
+    """Dense bf16 head_dim 128: the first chunk attention clears the workspace's counters on
+    the call's stream, later ones do not; every chunk call passes the workspace geometry;
+    recache attention never gets it (its calls are not split)."""
+    kw = dict(dtype="bf16", head_dim=128, heads=3, tokens_per_frame=100, window_frames=5)
+    h, size = _create(fake, **kw)
+    blocks, cache_keys, n = 3 * 2, 8 * 100, 300
+    assert size == 2 * 2 * 8 * 100 * 3 * 128 * 2 + _split_workspace(3, n, cache_keys, 256)
+    fake.llfake_reset()
+    for i in range(3):
+        assert fake.ll_attn_chunk(h, 0, P, P, P, P, None) == 0
+    recs = _records(fake)
+    assert [k for k, _ in recs] == [4, 0, 0, 0]
+    zero_addr, zero_bytes = recs[0][1][0], recs[0][1][1]
+    assert zero_addr == (1 << 20) + 2 * 2 * 8 * 100 * 3 * 128 * 2   # after both layers
+    assert zero_bytes == -(-blocks * 4 // 256) * 256
+    for _, f in recs[1:]:
+        assert f[16:20] == [1, blocks, 2 * min(256, blocks * (7 + 3)), 256]
+    assert fake.ll_cache_commit(h, 0, P, P, None) == 0
+    fake.llfake_reset()
+    assert fake.ll_recache(h, 0, P, P, P, P, P, P, 7, P, P, None) == 0
+    atts = [f for k, f in _records(fake) if k == 0]
+    assert len(atts) == 2 and all(f[16] == 0 for f in atts)
+    # a failed clear leaves the workspace uncleared: the next call clears it
+    h2, _ = _create(fake, **kw)
+    fake.llfake_reset()
+    fake.llfake_fail_next(1)
+    assert fake.ll_attn_chunk(h2, 0, P, P, P, P, None) == _lib.LL_EDEVICE
+    assert fake.ll_attn_chunk(h2, 0, P, P, P, P, None) == 0
+    assert [k for k, _ in _records(fake)] == [4, 0]
+    # fp32, head_dim 64 and FP4 caches have no workspace
+    for other in (dict(dtype="f32"), dict(head_dim=64), dict(kv_format="fp4")):
+        h3, size3 = _create(fake, **{**kw, **other})
+        fake.llfake_reset()
+        assert fake.ll_attn_chunk(h3, 0, P, P, P, P, None) == 0
+        (k0, f0), = _records(fake)
+        assert k0 == 0 and f0[16:19] == [0, 0, 0]
+        fake.ll_cache_destroy(h3)
+    fake.ll_cache_destroy(h)
+    fake.ll_cache_destroy(h2)
 
 
 def test_kv_quant_validation(fake):

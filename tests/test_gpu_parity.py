@@ -118,6 +118,26 @@ def test_layer_config_sampled():
     run_stream(shape, 20, compare={0, 1, 3, 4, 5, 19}, rows=rows, export_every=False)
 
 
+def test_three_head_share_sampled():
+    """The layer shape at 3 heads (one GPU's share of 12 heads over 4 sequence-parallel
+    ranks): 57 query blocks on a 256-CU device, so chunk attention runs split into equal key
+    ranges with up to 6 pieces per block that are merged on the device."""
+    shape = synth.shrink(synth.CONFIGS["layer"], name="share-h3", heads=3)
+    log("case: layer config at 3 heads, 8 chunks, sampled rows")
+    rows = sample_rows(shape.n_query, 64, seed=3)
+    run_stream(shape, 8, compare={0, 2, 4, 5, 7}, rows=rows, export_every=False)
+
+
+def test_split_with_many_pieces():
+    """One head of 1200 query rows over a 12-frame window of 400-token frames: five query
+    blocks on a many-CU device, so once the window is full every block's key tiles are
+    spread over dozens of workgroups and merged on the device (ragged tails: 4800 + 1200
+    keys are not multiples of the 128-key tile)."""
+    shape = synth.shrink(synth.CONFIGS["layer"], name="split-h1", heads=1, tokens_per_frame=400)
+    log("case: 1 head, 400-token frames, 8 chunks, all rows")
+    run_stream(shape, 8)
+
+
 def test_value_one_gives_one_and_determinism():
     import torch
     shape = synth.shrink(synth.CONFIGS["layer"], heads=2, tokens_per_frame=90, window_frames=4)

@@ -63,6 +63,11 @@ struct Params {
   DevSeg a, b;
   int32_t vis_mode, vT, vC, v_nsink, v_base, v_F;
   float c;           // softmax scale * log2(e)
+  // split mode (direct kernel): nt key tiles per block, the first `main` of them on the
+  // block's own workgroup, the rest spread over the n_wg - H * n_qblk spare workgroups
+  int32_t split, nt, main;
+  float* part;       // per-thread piece state: n_blocks main slots, then the tail slots
+  uint32_t* cnt;     // per-block arrival counters, zero between launches
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -485,53 +490,51 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* ld
                                            voff, 0, 0, 0);
 }
 
+// Work split. Plain: one workgroup per (head, query block), all of its key tiles. Split
+// (when there are fewer blocks than CUs): workgroup b < n_blocks runs block b's first
+// `main` key tiles, so the query blocks of a head still sweep the keys in step and share
+// them in L2; the remaining n_blocks x (nt - main) "tail" units (one key tile of one block
+// each), block-major, are cut into equal contiguous ranges over the spare workgroups. A
+// split block is finished by the last of its workgroups to arrive: each writes its
+// unnormalised state (O, running max, running sum) to a workspace slot and bumps the
+// block's counter; the one that sees the count complete merges the slots (main piece
+// first, then the tail pieces in range order) and stores O. No workgroup ever waits on
+// another.
+template <int NW>
+struct SplitState {
+  static constexpr int REGS = 66;               // 64 O values, running max, running sum
+  static constexpr int SLOT_FLOATS = REGS * NW * 64;
+  static_assert(NW != 8 || SLOT_FLOATS * 4 == kSplitSlotBytes, "slot size");
+};
+
+// first unit of range g, and the range holding unit u, for U units over G ranges
+__device__ __forceinline__ int64_t range_start(int64_t g, int64_t U, int64_t G) { return g * U / G; }
+__device__ __forceinline__ int64_t range_of(int64_t u, int64_t U, int64_t G) { return ((u + 1) * G - 1) / U; }
+
 template <int NW, int SUB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_direct_kernel(Params p) {
   constexpr int D = 128;
   using T = DtCfg<SUB>;
+  using SS = SplitState<NW>;
   constexpr int DT_TILE = T::TILE, DT_BUF = T::BUF, DT_LDS = T::LDS, TR = T::ROWS;
   constexpr int IPW = DT_TILE / 1024 / NW;  // direct loads per wave per tensor per tile
   static_assert(IPW * NW * 1024 == DT_TILE, "tile must split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_last;
 
+  // XCD-aware order: workgroup ids are dealt round-robin over the 8 XCDs; each XCD gets a
+  // contiguous range of logical ids, so the query blocks of one head share an L2
   const int G = p.n_wg;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, idx = bid >> 3;
   const int qd = G >> 3, rm = G & 7;
-  const int tile_id = (xcd < rm ? xcd * (qd + 1) : rm * (qd + 1) + (xcd - rm) * qd) + idx;
-  const int h = tile_id / p.n_qblk;
-  const int qblk = p.n_qblk - 1 - (tile_id % p.n_qblk);
+  const int g = (xcd < rm ? xcd * (qd + 1) : rm * (qd + 1) + (xcd - rm) * qd) + idx;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int row0 = qblk * (NW * 32);
-  const int row = row0 + wave * 32 + l32;
-  const int lim = row_limit(p, row < p.nq ? row : p.nq - 1);
-  const int wave_min_lim = row_limit(p, min(row0 + wave * 32, p.nq - 1));
-  const int kend = row_limit(p, min(row0 + NW * 32 - 1, p.nq - 1));
-  // tiles per segment; in block-causal mode only segment A holds keys and the last visible
-  // key of the block bounds the loop
   const int na = p.a.n;
-  const int ntA = ((p.vis_mode == 0 ? na : min(na, kend)) + TR - 1) / TR;
-  const int ntB = p.vis_mode == 0 ? (p.b.n + TR - 1) / TR : 0;
-  const int ntiles = ntA + ntB;
-
-  bf16x8_t qreg[D / 16];
-  {
-    const uint16_t* qp = p.q + int64_t(row < p.nq ? row : 0) * p.q_row + h * D + 8 * hi;
-#pragma unroll
-    for (int ss = 0; ss < D / 16; ++ss) {
-      const uint4 x = row < p.nq ? *reinterpret_cast<const uint4*>(qp + 16 * ss) : make_uint4(0, 0, 0, 0);
-      qreg[ss] = __builtin_bit_cast(bf16x8_t, x);
-    }
-  }
-  f32x16_t oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16_t{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
 
   // LDS read lane bases. K (A operand of S^T = K Q^T): row kb*32 + l32, logical chunk
   // 2ss + hi -> one base per ss. V (A operand of O^T = V^T P^T, via the transposing read):
@@ -564,104 +567,243 @@ void attn_bf16_direct_kernel(Params p) {
   for (int i = tid; i < DT_LDS / 16; i += NW * 64) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  auto issue = [&](int t, uint8_t* buf) {
-    const bool inA = t < ntA;
-    const DevSeg& sg = inA ? p.a : p.b;
-    const int r0 = (inA ? t : t - ntA) * TR;                  // first row of the tile in the segment
-    const int64_t rp = sg.row_stride * 2;                      // row pitch in bytes
-    const uint8_t* kb0 = sg.k + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
-    const uint8_t* vb0 = sg.v + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
-    const int left = sg.n - r0;                                // rows of this segment from r0 on
-    const uint32_t bytes = left > 0 ? uint32_t(left - 1) * uint32_t(rp) + DT_ROW : 0u;
-    const __amdgpu_buffer_rsrc_t rk = rsrc(kb0, bytes), rv = rsrc(vb0, bytes);
-#pragma unroll
-    for (int n = 0; n < IPW; ++n) {
-      const uint32_t ro = uint32_t(lrow[n]) * uint32_t(rp);
-      lds_load16(rk, buf + (wave * IPW + n) * 1024, ro + (ck[n] << 4));
-      lds_load16(rv, buf + DT_TILE + (wave * IPW + n) * 1024, ro + (cv[n] << 4));
+  // split mode: tail units and spare workgroups
+  const int nblk = p.H * p.n_qblk;
+  const int tail = p.nt - p.main;
+  const int64_t UT = int64_t(nblk) * tail;
+  const int GS = G - nblk;
+  const bool spare = p.split && g >= nblk;
+  const int64_t u0 = spare ? range_start(g - nblk, UT, GS) : 0;
+  const int64_t u1 = spare ? range_start(g - nblk + 1, UT, GS) : 0;
+  int64_t u = u0;
+  bool single_done = false;
+
+  for (;;) {
+    // ---- next piece: block (h, qblk), key tiles [t0, t1) ----
+    int h, qblk, t0, t1, blk = 0, slot = 0;
+    bool whole;
+    if (spare) {
+      if (u >= u1) break;
+      blk = int(u / tail);
+      t0 = int(u - int64_t(blk) * tail);
+      t1 = p.main + int(min<int64_t>(tail, t0 + (u1 - u)));
+      t0 += p.main;
+      h = blk / p.n_qblk;
+      qblk = blk - h * p.n_qblk;
+      whole = false;
+      // tail piece (spare s, block b) -> slot n_blocks + s + b: along the unit order s and b
+      // never decrease and one of them grows at every new piece, so the slots are distinct
+      slot = g + blk;
+      u += t1 - t0;
+    } else if (p.split) {
+      if (single_done) break;
+      single_done = true;
+      blk = g;
+      h = blk / p.n_qblk;
+      qblk = blk - h * p.n_qblk;
+      t0 = 0;
+      t1 = p.main;
+      whole = false;
+      slot = blk;
+    } else {
+      if (single_done) break;
+      single_done = true;
+      h = g / p.n_qblk;
+      // heavy-first inside a head: later query blocks see more keys under the block-causal mask
+      qblk = p.n_qblk - 1 - (g % p.n_qblk);
+      t0 = 0;
+      t1 = -1;  // all of the block's tiles, set below
+      whole = true;
     }
-  };
 
-  issue(0, smem);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+    const int row0 = qblk * (NW * 32);
+    const int row = row0 + wave * 32 + l32;
+    const int lim = row_limit(p, row < p.nq ? row : p.nq - 1);
+    const int wave_min_lim = row_limit(p, min(row0 + wave * 32, p.nq - 1));
+    const int kend = row_limit(p, min(row0 + NW * 32 - 1, p.nq - 1));
+    // tiles per segment; in block-causal mode only segment A holds keys and the last visible
+    // key of the block bounds the loop
+    const int ntA = ((p.vis_mode == 0 ? na : min(na, kend)) + TR - 1) / TR;
+    const int ntB = p.vis_mode == 0 ? (p.b.n + TR - 1) / TR : 0;
+    if (t1 < 0) t1 = ntA + ntB;
 
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) issue(t + 1, smem + ((t + 1) & 1) * DT_BUF);
-#pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-    const uint8_t* kt = smem + (t & 1) * DT_BUF + u * BN * DT_ROW;
-    const uint8_t* vt = kt + DT_TILE;
-
-    f32x16_t s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
+    bf16x8_t qreg[D / 16];
+    {
+      const uint16_t* qp = p.q + int64_t(row < p.nq ? row : 0) * p.q_row + h * D + 8 * hi;
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kbase[ss] + kb * 32 * DT_ROW);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ss], s[kb], 0, 0, 0);
+        const uint4 x = row < p.nq ? *reinterpret_cast<const uint4*>(qp + 16 * ss) : make_uint4(0, 0, 0, 0);
+        qreg[ss] = __builtin_bit_cast(bf16x8_t, x);
       }
     }
+    f32x16_t oacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16_t{};
+    float m_run = -__builtin_inff();
+    float l_run = 0.f;
 
-    // mask: rows past the segment's end, and keys past this row's block-causal limit
-    const bool inA = t < ntA;
-    const int r0 = (inA ? t : t - ntA) * TR + u * BN;
-    const int seg_left = (inA ? na : p.b.n) - r0;
-    const int key0 = (inA ? 0 : na) + r0;                      // key index of the sub-tile's row 0
-    if (seg_left <= 0) continue;                               // a sub-tile wholly past the end
-    if (seg_left < BN || key0 + BN > wave_min_lim) {
+    auto issue = [&](int t, uint8_t* buf) {
+      const bool inA = t < ntA;
+      const DevSeg& sg = inA ? p.a : p.b;
+      const int r0 = (inA ? t : t - ntA) * TR;                  // first row of the tile in the segment
+      const int64_t rp = sg.row_stride * 2;                      // row pitch in bytes
+      const uint8_t* kb0 = sg.k + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
+      const uint8_t* vb0 = sg.v + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
+      const int left = sg.n - r0;                                // rows of this segment from r0 on
+      const uint32_t bytes = left > 0 ? uint32_t(left - 1) * uint32_t(rp) + DT_ROW : 0u;
+      const __amdgpu_buffer_rsrc_t rk = rsrc(kb0, bytes), rv = rsrc(vb0, bytes);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (kr >= seg_left || key0 + kr >= lim) s[kb][r] = -__builtin_inff();
-        }
-    }
+      for (int n = 0; n < IPW; ++n) {
+        const uint32_t ro = uint32_t(lrow[n]) * uint32_t(rp);
+        lds_load16(rk, buf + (wave * IPW + n) * 1024, ro + (ck[n] << 4));
+        lds_load16(rv, buf + DT_TILE + (wave * IPW + n) * 1024, ro + (cv[n] << 4));
+      }
+    };
 
-    bf16x8_t pb[2][2];
-    softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
-
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint8_t* a0 = vt + vbase[db] + (kb * 32 + 16 * j) * DT_ROW;
-          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16_t*)(a0));
-          const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16_t*)(a0 + 8 * DT_ROW));
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][j], oacc[db], 0, 0, 0);
-        }
-    }
-    }
-
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of tile t+1 have landed
+    issue(t0, smem + (t0 & 1) * DT_BUF);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
 
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
-                                                     false, false);
-    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
-  if (row < p.nq) {
-    const float inv = 1.0f / l_run;
-    uint16_t* op = p.o + int64_t(row) * p.q_row + h * D + 4 * hi;
+    for (int t = t0; t < t1; ++t) {
+      if (t + 1 < t1) issue(t + 1, smem + ((t + 1) & 1) * DT_BUF);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int u2 = 0; u2 < SUB; ++u2) {
+      const uint8_t* kt = smem + (t & 1) * DT_BUF + u2 * BN * DT_ROW;
+      const uint8_t* vt = kt + DT_TILE;
+
+      const bool inA = t < ntA;
+      const int r0 = (inA ? t : t - ntA) * TR + u2 * BN;       // first row of the sub-tile
+      const int seg_left = (inA ? na : p.b.n) - r0;
+      if (seg_left <= 0) continue;                              // sub-tile wholly past the end
+      const int key0 = (inA ? 0 : na) + r0;
+
+      f32x16_t s[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 u;
-        u.x = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-        u.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(op + db * 32 + 8 * g) = u;
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16_t{};
+#pragma unroll
+        for (int ss = 0; ss < D / 16; ++ss) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kbase[ss] + kb * 32 * DT_ROW);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ss], s[kb], 0, 0, 0);
+        }
       }
+
+      // mask: rows past the segment's end, and keys past this row's block-causal limit
+      if (seg_left < BN || key0 + BN > wave_min_lim) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kr = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (kr >= seg_left || key0 + kr >= lim) s[kb][r] = -__builtin_inff();
+          }
+      }
+
+      bf16x8_t pb[2][2];
+      softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
+
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint8_t* a0 = vt + vbase[db] + (kb * 32 + 16 * j) * DT_ROW;
+            const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16_t*)(a0));
+            const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16_t*)(a0 + 8 * DT_ROW));
+            const bf16x8_t a = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][j], oacc[db], 0, 0, 0);
+          }
+      }
+      }
+
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of tile t+1 have landed
+      __syncthreads();
+    }
+
+    if (!whole) {
+      // ---- split block: publish this piece, and merge if it is the block's last ----
+      // The piece state is stored and read back with agent-scope (L2-coherent) accesses, and
+      // the counter bump is preceded by one release fence (write-back of dirty L2 lines): no
+      // acquire fence, whose L2 invalidation would evict the K/V every other workgroup on
+      // the XCD is reusing. The merging workgroup reads only after its counter bump returned
+      // the completing count.
+      float* sp = p.part + int64_t(slot) * SS::SLOT_FLOATS + wave * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          __hip_atomic_store(sp + (db * 16 + i) * NW * 64, oacc[db][i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sp + 64 * NW * 64, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sp + 65 * NW * 64, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are complete
+      __syncthreads();
+      const int64_t bu0 = int64_t(blk) * tail;                   // the block's first tail unit
+      const int gs_first = int(range_of(bu0, UT, GS));
+      const int gs_last = int(range_of(bu0 + tail - 1, UT, GS));
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t old = __hip_atomic_fetch_add(p.cnt + blk, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const int last = int(old) == gs_last - gs_first + 1;   // main piece + tail pieces - 1
+        if (last) __hip_atomic_store(p.cnt + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+      }
+      __syncthreads();
+      if (!s_last) continue;
+      // merge: the main piece, then the tail pieces in range order (the result does not
+      // depend on which workgroup merges)
+      for (int gs = gs_first - 1; gs <= gs_last; ++gs) {
+        const int sl = gs < gs_first ? blk : nblk + gs + blk;
+        const float* rp = p.part + int64_t(sl) * SS::SLOT_FLOATS + wave * 64 + lane;
+        auto ld = [&](int r) {
+          return __hip_atomic_load(rp + r * NW * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        const float m_p = ld(64);
+        const float l_p = ld(65);
+        if (gs < gs_first) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] = ld(db * 16 + i);
+          m_run = m_p;
+          l_run = l_p;
+        } else {
+          const float mn = fmaxf(m_run, m_p);
+          const float fa = m_run == mn ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
+          const float fb = m_p == mn ? 1.0f : __builtin_amdgcn_exp2f(m_p - mn);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] = oacc[db][i] * fa + ld(db * 16 + i) * fb;
+          l_run = l_run * fa + l_p * fb;
+          m_run = mn;
+        }
+      }
+    }
+
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                       false, false);
+      l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (row < p.nq) {
+      const float inv = 1.0f / l_run;
+      uint16_t* op = p.o + int64_t(row) * p.q_row + h * D + 4 * hi;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          uint2 v2;
+          v2.x = pack_bf16x2(oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv);
+          v2.y = pack_bf16x2(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
+          *reinterpret_cast<uint2*>(op + db * 32 + 8 * gq) = v2;
+        }
+    }
   }
 }
 
@@ -757,9 +899,47 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
     // dense keys: direct-to-LDS staging; FP4 keys: register staging with fused dequant
     if (fp4) return launch_t<128, NW, true>(p, p.n_wg, s, err);
     // 8 waves x 32 rows per workgroup, 128 keys per barrier, 2 workgroup waves per SIMD
-    constexpr int DNW = 8, DSUB = 2;
+    constexpr int DNW = 8, DSUB = 2, TR = DtCfg<DSUB>::ROWS;
+    static_assert(DNW * 32 == kSplitRows && TR == kSplitKeys, "split workspace geometry");
     p.n_qblk = (a.nq + DNW * 32 - 1) / (DNW * 32);
-    p.n_wg = p.n_qblk * a.H;
+    const int blocks = p.n_qblk * a.H;
+    p.n_wg = blocks;
+    if (a.vis.mode == 0 && a.ws && a.n_cu > blocks && blocks <= a.ws_blocks) {
+      // Split when the best main/tail cut is clearly shorter than one whole block. Cost in
+      // key tiles, with kPieceCost tiles per piece for its prologue (Q load, first tile not
+      // overlapped) and its publish; a spare workgroup runs at most ceil(span/tail) + 1
+      // pieces. Measured on MI355X: 12 heads x 4680 rows (228 blocks) is faster whole, 3
+      // heads (57 blocks) about 4x faster split.
+      constexpr int64_t kPieceCost = 5;
+      const int nt = (p.a.n + TR - 1) / TR + (p.b.n + TR - 1) / TR;
+      const int64_t spare = a.n_cu - blocks;
+      int best_main = nt;
+      int64_t best = nt;
+      for (int m = 1; m < nt; ++m) {
+        const int64_t tail = nt - m;
+        const int64_t ut = int64_t(blocks) * tail;
+        const int64_t gs = ut < spare ? ut : spare;
+        const int64_t span = (ut + gs - 1) / gs;
+        const int64_t c_main = m + kPieceCost;
+        const int64_t c_spare = span + kPieceCost * ((span + tail - 1) / tail + 1);
+        const int64_t mk = c_main > c_spare ? c_main : c_spare;
+        if (mk < best) {
+          best = mk;
+          best_main = m;
+        }
+      }
+      const int64_t ut = int64_t(blocks) * (nt - best_main);
+      const int64_t gs = ut < spare ? ut : spare;
+      if (best_main < nt && best * 100 < int64_t(nt) * 85 && 2 * (blocks + gs) <= a.ws_slots) {
+        uint8_t* ws = static_cast<uint8_t*>(a.ws);
+        p.split = 1;
+        p.nt = nt;
+        p.main = best_main;
+        p.n_wg = int(blocks + gs);
+        p.cnt = reinterpret_cast<uint32_t*>(ws);
+        p.part = reinterpret_cast<float*>(ws + split_slots_offset(a.ws_blocks));
+      }
+    }
     return launch_direct<DNW, DSUB>(p, p.n_wg, s, err);
   }
   if (a.D == 64) {

@@ -202,6 +202,12 @@ __global__ __launch_bounds__(256) void export_kernel(ExportP p) {
   }
 }
 
+// workspace clearing: one 32-bit word per thread
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 int finish(char* err) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -309,6 +315,25 @@ int launch_export(const ExportArgs& a, void* stream, char* err) {
   hipLaunchKernelGGL(export_kernel, grid, dim3(block_for(a.H * p.row_bytes / 4)), 0,
                      static_cast<hipStream_t>(stream), p);
   return finish(err);
+}
+
+int launch_zero(void* p, int64_t bytes, void* stream, char* err) {
+  if (bytes <= 0) return 0;
+  if (bytes % 4 != 0 || (bytes / 4 + 255) / 256 >= (int64_t(1) << 31)) {
+    snprintf(err, 256, "zero fill of %lld bytes", (long long)bytes);
+    return 1;
+  }
+  const int64_t n = bytes / 4;
+  hipLaunchKernelGGL(zero_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint32_t*>(p), n);
+  return finish(err);
+}
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
 }
 
 }  // namespace ll

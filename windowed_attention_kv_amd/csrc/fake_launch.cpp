@@ -11,8 +11,8 @@
 namespace {
 
 struct Record {
-  int kind;              // 0 attention, 1 scatter, 2 quant, 3 export
-  int64_t f[16];
+  int kind;              // 0 attention, 1 scatter, 2 quant, 3 export, 4 zero
+  int64_t f[20];
 };
 
 std::vector<Record> g_log;
@@ -35,7 +35,8 @@ int launch_attention(const AttnArgs& a, void*, char* err) {
   if (maybe_fail(err)) return 1;
   Record r{0, {a.dtype, a.H, a.D, a.nq, a.seg[0].n, a.seg[0].fp4, a.seg[0].head_stride,
                a.seg[0].row_stride, a.seg[1].n, a.seg[1].head_stride, a.seg[1].row_stride,
-               a.vis.mode, a.vis.n_sink, a.vis.base, a.vis.F, a.vis.C}};
+               a.vis.mode, a.vis.n_sink, a.vis.base, a.vis.F, a.vis.C,
+               a.ws != nullptr, a.ws_blocks, a.ws_slots, a.n_cu}};
   g_log.push_back(r);
   return 0;
 }
@@ -62,6 +63,15 @@ int launch_export(const ExportArgs& a, void*, char* err) {
   return 0;
 }
 
+int launch_zero(void* p, int64_t bytes, void*, char* err) {
+  if (maybe_fail(err)) return 1;
+  Record r{4, {int64_t(reinterpret_cast<uintptr_t>(p)), bytes}};
+  g_log.push_back(r);
+  return 0;
+}
+
+int device_cu_count() { return 256; }
+
 }  // namespace ll
 
 extern "C" {
@@ -75,10 +85,10 @@ void llfake_fail_next(int n) { g_fail = n; }
 
 int llfake_count(void) { return int(g_log.size()); }
 
-// kind of record i (or -1) and its 16 integer fields
+// kind of record i (or -1) and its 20 integer fields
 int llfake_record(int i, int64_t* fields) {
   if (i < 0 || i >= int(g_log.size())) return -1;
-  for (int j = 0; j < 16; ++j) fields[j] = g_log[size_t(i)].f[j];
+  for (int j = 0; j < 20; ++j) fields[j] = g_log[size_t(i)].f[j];
   return g_log[size_t(i)].kind;
 }
 

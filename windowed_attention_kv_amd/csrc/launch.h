@@ -42,7 +42,20 @@ struct AttnArgs {
   KeySeg seg[2];
   Visibility vis;
   float scale = 0.f;
+  // optional workspace for the split (stream-K) schedule of mode-0 calls: ws_blocks 32-bit
+  // arrival counters (zero between launches), then ws_slots piece-state slots of
+  // kSplitSlotBytes each, from byte split_slots_offset(ws_blocks)
+  void* ws = nullptr;
+  int32_t ws_blocks = 0, ws_slots = 0;
+  int32_t n_cu = 0;         // compute units of the device
 };
+
+// bytes of one piece-state slot of the split schedule: 66 floats per thread of an 8-wave
+// workgroup (64 O values, running max, running sum)
+constexpr int64_t kSplitSlotBytes = int64_t(66) * 8 * 64 * 4;
+// query rows and key rows per unit of the split schedule (head_dim 128, bf16)
+constexpr int32_t kSplitRows = 256, kSplitKeys = 128;
+inline int64_t split_slots_offset(int64_t ws_blocks) { return (ws_blocks * 4 + 255) / 256 * 256; }
 
 // Copy (or FP4-quantise) frames of a [n_frames*T, H, D] token-major K/V pair into cache
 // slots. Source frame r goes to slot slot_of_rank(r):
@@ -94,5 +107,9 @@ int launch_attention(const AttnArgs& a, void* stream, char* err);
 int launch_scatter(const ScatterArgs& a, void* stream, char* err);
 int launch_quant(const QuantArgs& a, void* stream, char* err);
 int launch_export(const ExportArgs& a, void* stream, char* err);
+// zero `bytes` (a multiple of 4) at p with a kernel on the stream
+int launch_zero(void* p, int64_t bytes, void* stream, char* err);
+// compute units of the current device (0 if it cannot be queried)
+int device_cu_count();
 
 }  // namespace ll

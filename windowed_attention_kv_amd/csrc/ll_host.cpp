@@ -49,6 +49,11 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t k_off, v_off, ks_off, vs_off;  // byte offsets inside one layer
   size_t layer_bytes;
+  // workspace of the split attention schedule, after the last layer (dense bf16 head_dim
+  // 128 only): arrival counters for every (head, query block) of a chunk call, then two
+  // piece-state slots per workgroup of the largest split launch
+  size_t ws_bytes;
+  int32_t ws_blocks, ws_slots;
 };
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -89,7 +94,7 @@ ll_status check_desc(const ll_cache_desc* d) {
   return LL_OK;
 }
 
-Layout layout_of(const ll_cache_desc* d) {
+Layout layout_of(const ll_cache_desc* d, int n_cu) {
   const size_t slots = size_t(d->sink_frames) + d->window_frames;
   const size_t elems = slots * d->tokens_per_frame * d->num_heads * d->head_dim;
   Layout L{};
@@ -108,7 +113,23 @@ Layout layout_of(const ll_cache_desc* d) {
     L.ks_off = L.vs_off = 0;
     L.layer_bytes = 2 * pl;
   }
+  L.ws_bytes = 0;
+  L.ws_blocks = L.ws_slots = 0;
+  if (d->kv_format == LL_KV_DENSE && d->dtype == LL_BF16 && d->head_dim == 128 && n_cu > 0) {
+    const int64_t n = int64_t(d->chunk_frames) * d->tokens_per_frame;
+    const int64_t blocks = int64_t(d->num_heads) * ((n + ll::kSplitRows - 1) / ll::kSplitRows);
+    const int64_t nt = (int64_t(slots) * d->tokens_per_frame + ll::kSplitKeys - 1) / ll::kSplitKeys +
+                       (n + ll::kSplitKeys - 1) / ll::kSplitKeys;
+    const int64_t G = std::min<int64_t>(n_cu, blocks * nt);
+    L.ws_blocks = int32_t(blocks);
+    L.ws_slots = int32_t(2 * G);
+    L.ws_bytes = size_t(ll::split_slots_offset(blocks) + 2 * G * ll::kSplitSlotBytes);
+  }
   return L;
+}
+
+size_t total_bytes(const ll_cache_desc* d, const Layout& L) {
+  return L.layer_bytes * size_t(d->num_layers) + L.ws_bytes;
 }
 
 }  // namespace
@@ -119,6 +140,8 @@ struct ll_cache {
   uint8_t* mem;
   size_t bytes;
   float scale;
+  int n_cu;
+  bool ws_ready;                // split-schedule counters zeroed (on the calls' stream)
   std::vector<int64_t> frames;  // frames committed per layer
 };
 
@@ -212,7 +235,7 @@ extern "C" {
 ll_status ll_cache_size(const ll_cache_desc* desc, size_t* device_bytes) {
   if (ll_status s = check_desc(desc)) return s;
   if (!device_bytes) return fail(LL_EINVAL, "device_bytes is NULL");
-  *device_bytes = layout_of(desc).layer_bytes * size_t(desc->num_layers);
+  *device_bytes = total_bytes(desc, layout_of(desc, ll::device_cu_count()));
   return ok();
 }
 
@@ -222,8 +245,9 @@ ll_status ll_cache_create(const ll_cache_desc* desc, void* device_mem, size_t de
   if (!out) return fail(LL_EINVAL, "out is NULL");
   if (!device_mem) return fail(LL_EINVAL, "device_mem is NULL");
   if (!aligned(device_mem, kAlign)) return fail(LL_EINVAL, "device_mem is not 256-byte aligned");
-  const Layout L = layout_of(desc);
-  const size_t need = L.layer_bytes * size_t(desc->num_layers);
+  const int n_cu = ll::device_cu_count();
+  const Layout L = layout_of(desc, n_cu);
+  const size_t need = total_bytes(desc, L);
   if (device_bytes < need)
     return fail(LL_EINVAL, "device_bytes %zu < required %zu", device_bytes, need);
   ll_cache* c = new (std::nothrow) ll_cache;
@@ -234,6 +258,8 @@ ll_status ll_cache_create(const ll_cache_desc* desc, void* device_mem, size_t de
   c->bytes = device_bytes;
   c->scale = desc->softmax_scale > 0.f ? desc->softmax_scale
                                        : float(1.0 / std::sqrt(double(desc->head_dim)));
+  c->n_cu = n_cu;
+  c->ws_ready = false;
   c->frames.assign(size_t(desc->num_layers), 0);
   *out = c;
   return ok();
@@ -270,6 +296,20 @@ ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const voi
   a.seg[1] = input_segment(d, k, v, n);
   a.scale = cache->scale;
   char msg[256] = "";
+  if (cache->L.ws_bytes) {
+    uint8_t* ws = cache->mem + cache->L.layer_bytes * size_t(d.num_layers);
+    if (!cache->ws_ready) {
+      if (ll_status s = device_status(
+              ll::launch_zero(ws, ll::split_slots_offset(cache->L.ws_blocks), stream, msg),
+              "workspace init", msg))
+        return s;
+      cache->ws_ready = true;
+    }
+    a.ws = ws;
+    a.ws_blocks = cache->L.ws_blocks;
+    a.ws_slots = cache->L.ws_slots;
+    a.n_cu = cache->n_cu;
+  }
   return device_status(ll::launch_attention(a, stream, msg), "attention launch", msg) ?: ok();
 }
 
