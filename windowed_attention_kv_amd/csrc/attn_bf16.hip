@@ -9,23 +9,23 @@
 // the block-causal limit of the recache prefill (launch.h, Visibility).
 //
 // Design (MI355X-first, not a port of any listed design):
-//  * one workgroup = NW waves x 32 query rows of one head; a wave keeps its 32 rows of Q in
-//    registers as the B operand of v_mfma_f32_32x32x16_bf16 and computes S^T = K Q^T, so each
-//    lane owns ONE query row: row max / row sum are in-lane reductions plus one
-//    v_permlane32_swap, never a cross-lane tree;
+//  * a wave keeps 32 query rows of Q in registers as the B operand of
+//    v_mfma_f32_32x32x16_bf16 and computes S^T = K Q^T, so each lane owns ONE query row: row
+//    max / row sum are in-lane reductions plus one v_permlane32_swap, never a cross-lane tree;
 //  * P^T goes straight from the S accumulator into the B operand of O^T = V^T P^T (no LDS
-//    round trip); V^T is read from LDS where the tile is stored transposed, with the keys of
-//    each 16-key group permuted so that one 16-byte read gives a lane its 8 keys;
-//  * K and V tiles of 64 keys are staged through LDS, double-buffered, one barrier per tile,
-//    with XOR-swizzled 16-byte columns; global loads are 16-byte (dense) and coalesced;
-//  * FP4 cache tiles are dequantised exactly while being written to LDS, so the MFMA inner
-//    loop is identical for both cache formats ("LongLive 2.0" distributed-inference page,
-//    NVFP4 and KV cache section: fused dequantisation);
+//    round trip);
 //  * online softmax in the exp2 domain with a lazy rescale: the running max only moves when a
 //    tile's max exceeds it by more than 2^8, so the O rescale (64 multiplies per lane) is
 //    rare; softmax is shift-invariant, so this changes rounding only;
+//  * FP4 cache tiles are dequantised exactly while being written to LDS, so the MFMA inner
+//    loop is identical for both cache formats ("LongLive 2.0" distributed-inference page,
+//    NVFP4 and KV cache section: fused dequantisation);
 //  * workgroups are mapped so that each XCD (own L2) works on a contiguous range of
 //    (head, query block) tiles: the query blocks of one head share their K/V in one L2.
+// Two kernels: attn_bf16_direct_kernel (head_dim 128: 8 waves, 128-key tiles loaded straight
+// into LDS, V read with transposing LDS reads, optional split schedule for calls with fewer
+// query blocks than CUs) and attn_bf16_kernel (head_dim 64: 4 waves, 64-key tiles staged
+// through registers and stored transposed).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -511,7 +511,7 @@ struct SplitState {
 __device__ __forceinline__ int64_t range_start(int64_t g, int64_t U, int64_t G) { return g * U / G; }
 __device__ __forceinline__ int64_t range_of(int64_t u, int64_t U, int64_t G) { return ((u + 1) * G - 1) / U; }
 
-template <int NW, int SUB>
+template <int NW, int SUB, bool FP4>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_direct_kernel(Params p) {
   constexpr int D = 128;
@@ -642,8 +642,47 @@ void attn_bf16_direct_kernel(Params p) {
     float m_run = -__builtin_inff();
     float l_run = 0.f;
 
+    // FP4 cache tiles (segment A under FP4) are staged through registers instead: thread
+    // tid holds row tid/4, elements 32*(tid%4).. of the tile -- 16 packed bytes and 2 scale
+    // bytes per tensor -- and dequant_store() writes them as bf16 into the same swizzled
+    // layout the direct loads produce.
+    uint4 kq = make_uint4(0, 0, 0, 0), vq = make_uint4(0, 0, 0, 0);
+    uint32_t kqs = 0, vqs = 0;
+    const int fr = tid >> 2, fq = tid & 3;
+    auto dequant_store = [&](uint8_t* buf, int v_off, int row_mask) {
+      const int rsw_k = fr & 15, rsw_v = (fr & 3) << 2;
+      const int wr = fr & row_mask;
+      const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w}, vw[4] = {vq.x, vq.y, vq.z, vq.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int lc = 4 * fq + c;                            // logical 16-byte chunk (8 elements)
+        const uint4 kd = dequant8(kw[c], (kqs >> (8 * (c >> 1))) & 0xFF);
+        const uint4 vd = dequant8(vw[c], (vqs >> (8 * (c >> 1))) & 0xFF);
+        *reinterpret_cast<uint4*>(buf + wr * DT_ROW + ((lc ^ rsw_k) << 4)) = kd;
+        *reinterpret_cast<uint4*>(buf + v_off + wr * DT_ROW + ((lc ^ rsw_v) << 4)) = vd;
+      }
+    };
+
     auto issue = [&](int t, uint8_t* buf) {
       const bool inA = t < ntA;
+      if constexpr (FP4) {
+        if (inA) {
+          const int r0 = t * TR;
+          const int64_t e0 = h * p.a.head_stride + int64_t(r0) * p.a.row_stride;
+          const int left = p.a.n - r0;
+          const uint32_t pbytes = left > 0 ? uint32_t(left) * (D / 2) : 0u;
+          const __amdgpu_buffer_rsrc_t rk = rsrc(p.a.k + e0 / 2, pbytes), rv = rsrc(p.a.v + e0 / 2, pbytes);
+          const __amdgpu_buffer_rsrc_t rks = rsrc(p.a.ks + e0 / 16, pbytes / 8);
+          const __amdgpu_buffer_rsrc_t rvs = rsrc(p.a.vs + e0 / 16, pbytes / 8);
+          const uint32_t off = uint32_t(fr) * (D / 2) + fq * 16;
+          kq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+          vq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+          const uint32_t soff = uint32_t(fr) * (D / 16) + fq * 2;
+          kqs = __builtin_amdgcn_raw_buffer_load_b16(rks, soff, 0, 0);
+          vqs = __builtin_amdgcn_raw_buffer_load_b16(rvs, soff, 0, 0);
+          return;
+        }
+      }
       const DevSeg& sg = inA ? p.a : p.b;
       const int r0 = (inA ? t : t - ntA) * TR;                  // first row of the tile in the segment
       const int64_t rp = sg.row_stride * 2;                      // row pitch in bytes
@@ -661,6 +700,7 @@ void attn_bf16_direct_kernel(Params p) {
     };
 
     issue(t0, smem + (t0 & 1) * DT_BUF);
+    if (FP4 && t0 < ntA) dequant_store(smem + (t0 & 1) * DT_BUF, DT_TILE, TR - 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -674,7 +714,9 @@ void attn_bf16_direct_kernel(Params p) {
       const bool inA = t < ntA;
       const int r0 = (inA ? t : t - ntA) * TR + u2 * BN;       // first row of the sub-tile
       const int seg_left = (inA ? na : p.b.n) - r0;
-      if (seg_left <= 0) continue;                              // sub-tile wholly past the end
+      // a sub-tile wholly past the end is skipped (FP4: computed fully masked instead, so the
+      // dequantisation below stays in one basic block with the QK products)
+      if (!FP4 && seg_left <= 0) continue;
       const int key0 = (inA ? 0 : na) + r0;
 
       f32x16_t s[2];
@@ -685,6 +727,16 @@ void attn_bf16_direct_kernel(Params p) {
         for (int ss = 0; ss < D / 16; ++ss) {
           const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kbase[ss] + kb * 32 * DT_ROW);
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ss], s[kb], 0, 0, 0);
+        }
+      }
+      if constexpr (FP4) {
+        // next tile's FP4 data -> bf16 while the QK products run; when the next tile is not
+        // FP4 (or past the piece) the stores go to a 16 KB scratch area above the two
+        // buffers instead (K and V rows folded onto 64 rows), so no branch is needed
+        if (u2 == SUB - 1) {
+          const bool real = t + 1 < t1 && t + 1 < ntA;
+          dequant_store(real ? smem + ((t + 1) & 1) * DT_BUF : smem + 2 * DT_BUF,
+                        real ? DT_TILE : 0, real ? TR - 1 : BN - 1);
         }
       }
 
@@ -807,10 +859,10 @@ void attn_bf16_direct_kernel(Params p) {
   }
 }
 
-template <int NW, int SUB>
+template <int NW, int SUB, bool FP4>
 int launch_direct(const Params& p, int grid, hipStream_t stream, char* err) {
-  auto kern = attn_bf16_direct_kernel<NW, SUB>;
-  constexpr int DT_LDS = DtCfg<SUB>::LDS;
+  auto kern = attn_bf16_direct_kernel<NW, SUB, FP4>;
+  constexpr int DT_LDS = DtCfg<SUB>::LDS + (FP4 ? BN * DT_ROW : 0);
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -896,9 +948,9 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp4 = p.a.fp4 != 0;
   if (a.D == 128) {
-    // dense keys: direct-to-LDS staging; FP4 keys: register staging with fused dequant
-    if (fp4) return launch_t<128, NW, true>(p, p.n_wg, s, err);
-    // 8 waves x 32 rows per workgroup, 128 keys per barrier, 2 workgroup waves per SIMD
+    // 8 waves x 32 rows per workgroup, 128 keys per barrier, 2 workgroup waves per SIMD;
+    // dense tiles come in by direct-to-LDS loads, FP4 cache tiles through registers with the
+    // dequantisation fused into the LDS write
     constexpr int DNW = 8, DSUB = 2, TR = DtCfg<DSUB>::ROWS;
     static_assert(DNW * 32 == kSplitRows && TR == kSplitKeys, "split workspace geometry");
     p.n_qblk = (a.nq + DNW * 32 - 1) / (DNW * 32);
@@ -940,7 +992,8 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
         p.part = reinterpret_cast<float*>(ws + split_slots_offset(a.ws_blocks));
       }
     }
-    return launch_direct<DNW, DSUB>(p, p.n_wg, s, err);
+    return fp4 ? launch_direct<DNW, DSUB, true>(p, p.n_wg, s, err)
+               : launch_direct<DNW, DSUB, false>(p, p.n_wg, s, err);
   }
   if (a.D == 64) {
     return fp4 ? launch_t<64, NW, true>(p, p.n_wg, s, err) : launch_t<64, NW, false>(p, p.n_wg, s, err);
