@@ -273,6 +273,29 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     res["attention_steady"] = {"ms": round(ms, 4), "tflops": round(steady_flops / ms / 1e9, 1),
                                "frac_bf16_peak": round(steady_flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
                                "keys": 23400}
+    # one GPU's share of the heads under 4-way sequence parallelism: the layer shape at 3
+    # heads (57 query blocks on 256 CUs, so chunk attention runs with the split schedule)
+    Hs = 3
+    share_in = [tuple(t[:, :Hs].contiguous() for t in trip) for trip in inputs]
+    outs = torch.empty((n, Hs, D), dtype=torch.bfloat16, device="cuda")
+    cs = Cache(1, Hs, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
+               shape.window_frames)
+    for rep in range(2):
+        cs.reset()
+        tm = EventTimer(torch)
+        for c, (q, k, v) in enumerate(share_in):
+            s = tm.start()
+            cs.attn_chunk(0, q, k, v, out=outs)
+            tm.stop(s, "attn_steady" if c >= 4 else "attn_fill")
+            cs.commit(0, k, v)
+        torch.cuda.synchronize()
+    tot = tm.totals()
+    ms = tot["attn_steady"][0] / tot["attn_steady"][1]
+    share_flops = attn_flops(n, 23400, Hs, D)
+    res["share_3_heads_steady"] = {"ms": round(ms, 4), "tflops": round(share_flops / ms / 1e9, 1),
+                                   "frac_bf16_peak": round(share_flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                   "note": "3 of 12 heads (4-way sequence-parallel share), split schedule"}
+    del share_in, outs, cs
     # standalone quant of one 12-frame cache (K and V): 2 x 18720 x 1536 elements
     x = torch.randn((2 * 18720 * H, D), device="cuda").mul_(0.5).to(torch.bfloat16)
     pk = torch.empty((x.shape[0], D // 2), dtype=torch.uint8, device="cuda")
@@ -399,7 +422,7 @@ def main():
                      # Q and O (n x H x D bf16 each) + the visible keys' K and V: per launch the
                      # K/V bytes are 2 * keys * H * D * 2 = flops_per_launch / n
                      "algorithmic_bytes_per_launch": round(2 * n * H * D * 2 + attn_flops_launch / n),
-                     "kernel": "attn_bf16_direct_kernel<8,2>",
+                     "kernel": "attn_bf16_direct_kernel<8,2,false>",
                      "avg_launch_ms": round(attn_ms, 4),
                      "avg_flops_per_launch": attn_flops_launch},
         "rows": {"commit": {"avg_launch_ms": round(commit_ms, 5), "bytes": commit_bytes,

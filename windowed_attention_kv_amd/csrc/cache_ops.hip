@@ -120,14 +120,16 @@ __global__ __launch_bounds__(256) void scatter_dense_kernel(ScatterP p, int32_t 
 }
 
 // fp4: one thread per 64 elements (4 scale blocks) of a (token, head) row, one workgroup per
-// 8 token rows and K|V: 32 packed bytes and one 4-byte scale word per thread. D % 64 == 0.
+// kFp4Rows token rows and K|V: 32 packed bytes and one 4-byte scale word per thread.
+// D % 64 == 0.
+constexpr int kFp4Rows = 8;
 __global__ __launch_bounds__(256) void scatter_fp4_kernel(ScatterP p, int32_t n_units, int32_t units,
                                                           float inv_units, float inv_t, int32_t gph_log2) {
   const int which = blockIdx.y;
   const int64_t head_rows = int64_t(p.slots) * p.T;
-  const int32_t tr0 = p.row0 + blockIdx.x * 8;
+  const int32_t tr0 = p.row0 + blockIdx.x * kFp4Rows;
   const int32_t nrows = n_units / units;
-  const int32_t nr = min(8, p.row0 + nrows - tr0);
+  const int32_t nr = min(kFp4Rows, p.row0 + nrows - tr0);
   for (int32_t i = threadIdx.x; i < nr * units; i += blockDim.x) {
     const int32_t rl = i / units, g = i - rl * units;
     const int32_t tr = tr0 + rl;
@@ -260,7 +262,7 @@ int launch_scatter(const ScatterArgs& a, void* stream, char* err) {
     p.row0 = r0;
     const int32_t n_units = min(rows_per_launch, n_rows - r0) * units;
     if (a.fp4) {
-      const int blocks = (n_units / units + 7) / 8;
+      const int blocks = (n_units / units + kFp4Rows - 1) / kFp4Rows;
       hipLaunchKernelGGL(scatter_fp4_kernel, dim3(blocks, 2), dim3(256), 0, s, p, n_units, units,
                          1.0f / float(units), inv_t, gph == 2 ? 1 : 0);
     } else {
