@@ -207,6 +207,69 @@ def stack_row(torch, shape, Cache, attn_flops, kv_format, pool):
             "work": f"{L} layers x {steps} steps x {chunks} chunks, {kv_format} KV, attention + commits"}
 
 
+def composite_row(torch, shape, Cache, attn_flops, pool):
+    """The interactive composite: the dense stack stream (30 layers x 4 steps x 80 chunks)
+    with a prompt switch at every sixth of the stream (six prompts, five switches), where all
+    30 layers are recached with a new 512-token prompt before the next chunk. Timed end to end
+    with events; inputs cycle through resident synthetic sets."""
+    L, steps, chunks, n_text = 30, 4, 80, 512
+    n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
+    C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
+    switches = [round(chunks * j / 6) for j in range(1, 6)]
+    cache = Cache(L, H, D, T, C, S, W)
+    out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+    rows = (S + W) * T
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    big = [(torch.randn((rows, H, D), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+           for _ in range(4)]
+    txt = [(torch.randn((n_text, H, D), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+           for _ in range(2)]
+    o = torch.empty_like(big[0])
+    ox = torch.empty_like(big[0])
+    flops = 0.0
+    qrows = 0
+    for c in range(chunks):
+        flops += L * steps * attn_flops(n, visible_keys(c, C, S, W, T), H, D)
+        qrows += L * steps * n
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    i = 0
+    for c in range(chunks):
+        if c in switches:
+            held = cache.held_rows(0)
+            for layer in range(L):
+                cache.recache(layer, big[0][:held], big[1][:held], big[2][:held], big[3][:held],
+                              txt[0], txt[1], out=o[:held], out_x=ox[:held])
+        for st in range(steps):
+            for layer in range(L):
+                q, k, v = pool[i % len(pool)]
+                i += 1
+                cache.attn_chunk(layer, q, k, v, out=out)
+                if st == steps - 1:
+                    cache.commit(layer, k, v)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    # recache flops: held frames in groups of one chunk, group j seeing groups 0..j (block
+    # causal), plus the cross-attention to n_text keys
+    for c in switches:
+        F = c * C
+        held_frames = min(F, S) + min(max(F - S, 0), W)
+        groups = held_frames // C
+        self_pairs = sum(C * T * (j + 1) * C * T for j in range(groups))
+        flops += L * (self_pairs + held_frames * T * n_text) * H * 4 * D
+        qrows += L * 2 * held_frames * T
+    return {"ms": round(ms, 2), "query_rows": qrows, "query_tokens_per_s": round(qrows / ms * 1e3, 1),
+            "tflops": round(flops / ms / 1e9, 1),
+            "frac_bf16_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "pflop": round(flops / 1e15, 4), "switches_at_chunk": switches,
+            "work": (f"{L} layers x {steps} steps x {chunks} chunks, dense KV, attention + commits, "
+                     f"{len(switches)} prompt switches each recaching {L} layers ({n_text} text tokens)")}
+
+
 def commit_batch_row(torch, shape, Cache, kv_format, k, v):
     """Per-commit time of 30 back-to-back commits (one per layer of a 30-layer cache), the
     pattern of the stack workload; events bracket each batch of 30."""
@@ -273,6 +336,31 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     res["attention_steady"] = {"ms": round(ms, 4), "tflops": round(steady_flops / ms / 1e9, 1),
                                "frac_bf16_peak": round(steady_flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
                                "keys": 23400}
+    # the chunk's text cross-attention (512 text tokens) fused into the same launch
+    gx = torch.Generator(device="cuda")
+    gx.manual_seed(17)
+    qx = (torch.randn((n, H, D), generator=gx, device="cuda") * 0.5).to(torch.bfloat16)
+    ktx = (torch.randn((512, H, D), generator=gx, device="cuda") * 0.5).to(torch.bfloat16)
+    vtx = (torch.randn((512, H, D), generator=gx, device="cuda") * 0.5).to(torch.bfloat16)
+    ox = torch.empty_like(out)
+    tm = EventTimer(torch)
+    for rep in range(2):
+        cd.reset()
+        for c, (q, k, v) in enumerate(inputs):
+            s = tm.start()
+            cd.attn_chunk_cross(0, q, k, v, qx, ktx, vtx, out=out, out_x=ox)
+            tm.stop(s, "fused_steady" if c >= 4 and rep > 0 else "fused_other")
+            cd.commit(0, k, v)
+    torch.cuda.synchronize()
+    tot = tm.totals()
+    ms_f = tot["fused_steady"][0] / tot["fused_steady"][1]
+    fused_flops = steady_flops + attn_flops(n, 512, H, D)
+    res["attention_cross_fused_steady"] = {
+        "ms": round(ms_f, 4), "tflops": round(fused_flops / ms_f / 1e9, 1),
+        "frac_bf16_peak": round(fused_flops / ms_f / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "cross_us_over_self_only": round((ms_f - res["attention_steady"]["ms"]) * 1e3, 1),
+        "note": "self (23400 keys) + text cross-attention (512 keys) in one launch"}
+    del qx, ktx, vtx, ox
     # one GPU's share of the heads under 4-way sequence parallelism: the layer shape at 3
     # heads (57 query blocks on 256 CUs, so chunk attention runs with the split schedule)
     Hs = 3
@@ -350,6 +438,7 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     pool = gen_inputs(torch, 8, n, H, D, 21, "cuda")
     res["stack_dense"] = stack_row(torch, shape, Cache, attn_flops, "dense", pool)
     res["stack_fp4"] = stack_row(torch, shape, Cache, attn_flops, "fp4", pool)
+    res["interactive_composite"] = composite_row(torch, shape, Cache, attn_flops, pool)
     return res
 
 

@@ -111,6 +111,22 @@ ll_status ll_cache_reset(ll_cache* cache);
 ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const void* k,
                         const void* v, void* o, void* stream);
 
+/* ll_attn_chunk plus the chunk's text cross-attention in the same launch. In every DiT block
+ * of the generator the self-attention over the frames is followed by a cross-attention of the
+ * same tokens to the prompt's text tokens ("LongLive" summary page, 方法 §1 KV 重缓存, which
+ * pairs the frames with the prompt through this cross-attention). Computes o exactly as
+ * ll_attn_chunk does, and
+ *   ox = softmax(scale * qx K_text^T) V_text over all n_text text keys (no mask),
+ * with qx, ox: [C*T, H, D] and k_text, v_text: [n_text, H, D], n_text >= 1, in the cache's
+ * dtype (the text K/V are never quantised). For a bf16 head_dim-128 cache both parts run in
+ * one kernel launch (the cross blocks take the compute units the self-attention leaves
+ * idle); otherwise as two launches on `stream`. Errors as ll_attn_chunk, plus LL_EINVAL for a
+ * NULL text pointer or an n_text out of range. */
+ll_status ll_attn_chunk_cross(ll_cache* cache, int32_t layer, const void* q, const void* k,
+                              const void* v, const void* qx, const void* k_text,
+                              const void* v_text, int32_t n_text, void* o, void* ox,
+                              void* stream);
+
 /* Append the chunk's K/V ([C*T, H, D], the final denoise step's values) as frames
  * F..F+C-1 (F = frames committed) and advance F by C. Frame f goes to slot f if f < S and
  * to slot S + (f-S) mod W otherwise; writing a window slot evicts the frame W earlier. One

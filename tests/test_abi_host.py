@@ -60,7 +60,7 @@ P = ctypes.c_void_p(1 << 24)  # aligned dummy device pointer
 
 def _records(f):
     out = []
-    buf = (ctypes.c_int64 * 20)()
+    buf = (ctypes.c_int64 * 24)()
     for i in range(f.llfake_count()):
         kind = f.llfake_record(i, buf)
         out.append((kind, list(buf)))
@@ -268,6 +268,28 @@ def test_split_workspace_is_cleared_once_and_passed_to_chunk_attention(fake):
         fake.ll_cache_destroy(h3)
     fake.ll_cache_destroy(h)
     fake.ll_cache_destroy(h2)
+
+
+def test_attn_chunk_cross_arguments(fake):
+    """ll_attn_chunk_cross passes the cross tensors to the same attention launch (text keys
+    token-major: row stride H*D), validates them first and changes no state on error."""
+    h, _ = _create(fake)
+    fake.llfake_reset()
+    assert fake.ll_attn_chunk_cross(h, 1, P, P, P, P, P, P, 77, P, P, None) == 0
+    (kind, f), = _records(fake)
+    assert kind == 0 and f[20:24] == [1, 1, 77, 2 * 64]
+    assert f[3] == 3 * 16 and f[11] == 0
+    assert fake.ll_attn_chunk(h, 1, P, P, P, P, None) == 0
+    assert _records(fake)[-1][1][20:23] == [0, 0, 0]
+    bad = [(None, P, P, 77, P), (P, None, P, 77, P), (P, P, None, 77, P), (P, P, P, 0, P),
+           (P, P, P, -3, P), (P, P, P, 77, None), (P, P, P, 1 << 30, P)]
+    for qx, kt, vt, nt, ox in bad:
+        fake.llfake_reset()
+        assert fake.ll_attn_chunk_cross(h, 1, P, P, P, qx, kt, vt, nt, P, ox, None) == _lib.LL_EINVAL
+        assert fake.llfake_count() == 0
+    assert fake.ll_attn_chunk_cross(h, 2, P, P, P, P, P, P, 77, P, P, None) == _lib.LL_EINVAL
+    assert _state(fake, h, 1, 9) == (0, [-1] * 9)
+    fake.ll_cache_destroy(h)
 
 
 def test_kv_quant_validation(fake):

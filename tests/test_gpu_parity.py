@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 from _parity import assert_close, log, sample_rows, to_np
+from oracle import attention as oatt
 from oracle import fp4 as ofp4
 from oracle import ring
 from oracle.model import LayerModel
@@ -276,3 +277,97 @@ def test_recache_config_sampled():
     log("case: recache config, sampled rows")
     rows = sample_rows(12 * shape.tokens_per_frame, 40, seed=3)
     _recache_case(shape, 10, n_text=512, rows=rows, after=1)
+
+
+def test_interactive_composite_small():
+    """The interactive pattern at a small shape: 2 layers x 2 denoise steps x 12 chunks with a
+    prompt switch (recache of both layers with new text K/V) before chunks 3, 6 and 9. Every
+    chunk output, every recache output and the final caches are checked against one oracle
+    model per layer."""
+    shape = synth.shrink(synth.CONFIGS["layer"], name="composite", heads=2, tokens_per_frame=64)
+    log("case: interactive composite, 2 layers, 12 chunks, switches at 3/6/9")
+    L, steps, switches, n_text = 2, 2, (3, 6, 9), 40
+    cache = _cache(shape, layers=L)
+    models = [_model(shape) for _ in range(L)]
+    for c in range(12):
+        if c in switches:
+            for layer in range(L):
+                n = len(models[layer].held()) * shape.tokens_per_frame
+                ins = synth.recache_inputs(shape, layer, n, n_text, salt=c)
+                q, k, v, qx, kt, vt = ins
+                o, ox = cache.recache(layer, *(t.torch("cuda") for t in ins))
+                ref_o, ref_ox = models[layer].recache(q.values, k.values, v.values, qx.values,
+                                                      kt.values, vt.values, k.bits, v.bits)
+                assert_close(to_np(o), ref_o, "bf16", f"switch {c} layer {layer} self")
+                assert_close(to_np(ox), ref_ox, "bf16", f"switch {c} layer {layer} cross")
+        for step in range(steps):
+            for layer in range(L):
+                q, k, v = synth.chunk_inputs(shape, layer, step, c)
+                tk, tv = k.torch("cuda"), v.torch("cuda")
+                o = cache.attn_chunk(layer, q.torch("cuda"), tk, tv)
+                assert_close(to_np(o), models[layer].attn_chunk(q.values, k.values, v.values),
+                             "bf16", f"chunk {c} step {step} layer {layer}")
+                if step == steps - 1:
+                    cache.commit(layer, tk, tv)
+                    models[layer].commit(k.values, v.values, k.bits, v.bits)
+    for layer in range(L):
+        _check_export(cache, models[layer], shape, layer)
+
+
+def _cross_stream(shape, n_chunks, n_text, kv_format="dense", compare=None, rows=None):
+    """Stream chunks through ll_attn_chunk_cross: o against the chunk oracle, ox against the
+    oracle's plain attention of qx over the text keys, and o bit-identical to ll_attn_chunk's
+    (the self part of the fused launch runs the same schedule)."""
+    import torch
+    cache = _cache(shape, kv_format)
+    model = _model(shape, kv_format)
+    for c in range(n_chunks):
+        q, k, v = synth.chunk_inputs(shape, 0, 0, c)
+        xs = synth.recache_inputs(shape, 0, shape.n_query, n_text, salt=100 + c)
+        qx, kt, vt = xs[3], xs[4], xs[5]
+        tq, tk, tv = q.torch("cuda"), k.torch("cuda"), v.torch("cuda")
+        o, ox = cache.attn_chunk_cross(0, tq, tk, tv, qx.torch("cuda"), kt.torch("cuda"),
+                                       vt.torch("cuda"))
+        o_plain = cache.attn_chunk(0, tq, tk, tv)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_plain), f"chunk {c}: fused self part differs from ll_attn_chunk"
+        if compare is None or c in compare:
+            r = rows if rows is not None else np.arange(shape.n_query)
+            assert_close(to_np(o)[r], model.attn_chunk(q.values, k.values, v.values, rows=r),
+                         shape.dtype, f"chunk {c} self")
+            ref_x = oatt.attention_rows(qx.values, kt.values, vt.values, model.scale, rows=r)
+            assert_close(to_np(ox)[r], ref_x, shape.dtype, f"chunk {c} cross")
+        cache.commit(0, tk, tv)
+        model.commit(k.values, v.values, k.bits, v.bits)
+
+
+@pytest.mark.parametrize("heads,T,n_text", [(3, 100, 77), (1, 400, 512), (2, 64, 1)])
+def test_attn_chunk_cross_fused(heads, T, n_text):
+    """bf16 head_dim 128: self and text cross-attention in one launch; (1 head, 400-token
+    frames) also runs the split schedule with the cross blocks after it."""
+    shape = synth.shrink(synth.CONFIGS["layer"], name=f"cross-h{heads}", heads=heads,
+                         tokens_per_frame=T)
+    log(f"case: fused cross-attention, {heads} heads, T={T}, {n_text} text keys")
+    _cross_stream(shape, 6, n_text)
+
+
+def test_attn_chunk_cross_other_shapes():
+    """head_dim 64 (bf16), fp32 and an FP4 cache: the same results through two launches
+    (head_dim 64, fp32) or the fused FP4 kernel."""
+    log("case: cross-attention, head_dim 64")
+    _cross_stream(synth.shrink(synth.CONFIGS["layer"], name="cross-d64", heads=2, head_dim=64,
+                               tokens_per_frame=72), 5, 50)
+    log("case: cross-attention, fp32")
+    _cross_stream(synth.shrink(synth.CONFIGS["tiny"], name="cross-f32"), 6, 20)
+    log("case: cross-attention, FP4 cache")
+    _cross_stream(synth.shrink(synth.CONFIGS["layer"], name="cross-fp4", heads=2,
+                               tokens_per_frame=64), 6, 64, kv_format="fp4")
+
+
+def test_attn_chunk_cross_layer_config_sampled():
+    """The layer shape with 512 text tokens: 228 self blocks leave 28 of 256 CUs for the
+    cross blocks; sampled rows on fill-up and steady chunks."""
+    shape = synth.CONFIGS["layer"]
+    log("case: fused cross-attention, layer config, sampled rows")
+    _cross_stream(shape, 6, 512, compare={0, 5}, rows=sample_rows(shape.n_query, 48, seed=5))
+

@@ -100,6 +100,20 @@ class Cache:
                                                  self._check(o, n, "o"), _stream(self.device)))
         return o
 
+    def attn_chunk_cross(self, layer, q, k, v, qx, k_text, v_text, out=None, out_x=None):
+        """attn_chunk plus the text cross-attention ox = softmax(scale qx K_text^T) V_text in
+        one call (one launch for bf16 head_dim 128). Returns (o, ox)."""
+        n = self.n_chunk
+        nt = k_text.shape[0]
+        o = self._empty(n) if out is None else out
+        ox = self._empty(n) if out_x is None else out_x
+        check(self._lib, self._lib.ll_attn_chunk_cross(
+            self.handle, layer, self._check(q, n, "q"), self._check(k, n, "k"),
+            self._check(v, n, "v"), self._check(qx, n, "qx"), self._check(k_text, nt, "k_text"),
+            self._check(v_text, nt, "v_text"), nt, self._check(o, n, "o"), self._check(ox, n, "ox"),
+            _stream(self.device)))
+        return o, ox
+
     def commit(self, layer, k, v):
         n = self.n_chunk
         check(self._lib, self._lib.ll_cache_commit(self.handle, layer, self._check(k, n, "k"),

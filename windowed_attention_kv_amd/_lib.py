@@ -17,8 +17,8 @@ STATUS_NAMES = {0: "LL_OK", 1: "LL_EINVAL", 2: "LL_ESTATE", 3: "LL_EUNSUPPORTED"
 
 # every symbol include/ll.h declares
 SYMBOLS = ["ll_cache_size", "ll_cache_create", "ll_cache_destroy", "ll_cache_reset",
-           "ll_attn_chunk", "ll_cache_commit", "ll_recache", "ll_kv_quant", "ll_cache_state",
-           "ll_cache_export", "ll_last_error"]
+           "ll_attn_chunk", "ll_attn_chunk_cross", "ll_cache_commit", "ll_recache", "ll_kv_quant",
+           "ll_cache_state", "ll_cache_export", "ll_last_error"]
 
 
 class CacheDesc(ctypes.Structure):
@@ -52,6 +52,7 @@ def _declare(lib):
     lib.ll_cache_destroy.argtypes = [_P]
     lib.ll_cache_reset.argtypes = [_P]
     lib.ll_attn_chunk.argtypes = [_P, _I32, _P, _P, _P, _P, _P]
+    lib.ll_attn_chunk_cross.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]
     lib.ll_cache_commit.argtypes = [_P, _I32, _P, _P, _P]
     lib.ll_recache.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]
     lib.ll_kv_quant.argtypes = [_P, _I64, _I32, _P, _P, _P]

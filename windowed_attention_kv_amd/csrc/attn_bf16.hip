@@ -64,8 +64,14 @@ struct Params {
   int32_t vis_mode, vT, vC, v_nsink, v_base, v_F;
   float c;           // softmax scale * log2(e)
   // split mode (direct kernel): nt key tiles per block, the first `main` of them on the
-  // block's own workgroup, the rest spread over the n_wg - H * n_qblk spare workgroups
+  // block's own workgroup, the rest spread over the n_self_wg - H * n_qblk spare workgroups
   int32_t split, nt, main;
+  // fused cross-attention (direct kernel, mode 0): workgroups n_self_wg.. run whole blocks of
+  // ox = softmax(scale qx K_x^T) V_x over the x segment
+  int32_t n_self_wg;
+  const uint16_t* qx;
+  uint16_t* ox;
+  DevSeg x;
   float* part;       // per-thread piece state: n_blocks main slots, then the tail slots
   uint32_t* cnt;     // per-block arrival counters, zero between launches
 };
@@ -525,16 +531,20 @@ void attn_bf16_direct_kernel(Params p) {
 
   // XCD-aware order: workgroup ids are dealt round-robin over the 8 XCDs; each XCD gets a
   // contiguous range of logical ids, so the query blocks of one head share an L2
+  // (ids from n_self_wg on are the fused cross-attention workgroups: they keep their ids, so
+  // they are dispatched after every self-attention workgroup)
   const int G = p.n_wg;
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int qd = G >> 3, rm = G & 7;
-  const int g = (xcd < rm ? xcd * (qd + 1) : rm * (qd + 1) + (xcd - rm) * qd) + idx;
+  int g = bid;
+  if (bid < p.n_self_wg) {
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int qd = p.n_self_wg >> 3, rm = p.n_self_wg & 7;
+    g = (xcd < rm ? xcd * (qd + 1) : rm * (qd + 1) + (xcd - rm) * qd) + idx;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int na = p.a.n;
 
   // LDS read lane bases. K (A operand of S^T = K Q^T): row kb*32 + l32, logical chunk
   // 2ss + hi -> one base per ss. V (A operand of O^T = V^T P^T, via the transposing read):
@@ -571,18 +581,33 @@ void attn_bf16_direct_kernel(Params p) {
   const int nblk = p.H * p.n_qblk;
   const int tail = p.nt - p.main;
   const int64_t UT = int64_t(nblk) * tail;
-  const int GS = G - nblk;
-  const bool spare = p.split && g >= nblk;
+  const int GSELF = p.n_self_wg;
+  const int GS = GSELF - nblk;
+  const bool xwg = g >= GSELF;                 // a fused cross-attention workgroup
+  const bool spare = !xwg && p.split && g >= nblk;
   const int64_t u0 = spare ? range_start(g - nblk, UT, GS) : 0;
   const int64_t u1 = spare ? range_start(g - nblk + 1, UT, GS) : 0;
   int64_t u = u0;
+  // cross workgroups: an equal contiguous range of whole cross blocks each
+  const int GX = G - GSELF;
+  int bx = xwg ? int(range_start(g - GSELF, nblk, GX)) : 0;
+  const int bx1 = xwg ? int(range_start(g - GSELF + 1, nblk, GX)) : 0;
   bool single_done = false;
 
   for (;;) {
     // ---- next piece: block (h, qblk), key tiles [t0, t1) ----
     int h, qblk, t0, t1, blk = 0, slot = 0;
-    bool whole;
-    if (spare) {
+    bool whole, xjob = false;
+    if (xwg) {
+      if (bx >= bx1) break;
+      blk = bx++;
+      h = blk / p.n_qblk;
+      qblk = blk - h * p.n_qblk;
+      t0 = 0;
+      t1 = -1;
+      whole = true;
+      xjob = true;
+    } else if (spare) {
       if (u >= u1) break;
       blk = int(u / tail);
       t0 = int(u - int64_t(blk) * tail);
@@ -616,20 +641,25 @@ void attn_bf16_direct_kernel(Params p) {
       whole = true;
     }
 
+    // the piece's key segments: self = (cache, own chunk), cross = (x, none)
+    const DevSeg& SA = xjob ? p.x : p.a;
+    const int na = SA.n;
+    const int nb = xjob ? 0 : p.b.n;
     const int row0 = qblk * (NW * 32);
     const int row = row0 + wave * 32 + l32;
-    const int lim = row_limit(p, row < p.nq ? row : p.nq - 1);
-    const int wave_min_lim = row_limit(p, min(row0 + wave * 32, p.nq - 1));
-    const int kend = row_limit(p, min(row0 + NW * 32 - 1, p.nq - 1));
+    const int lim = xjob ? na : row_limit(p, row < p.nq ? row : p.nq - 1);
+    const int wave_min_lim = xjob ? na : row_limit(p, min(row0 + wave * 32, p.nq - 1));
+    const int kend = xjob ? na : row_limit(p, min(row0 + NW * 32 - 1, p.nq - 1));
     // tiles per segment; in block-causal mode only segment A holds keys and the last visible
     // key of the block bounds the loop
     const int ntA = ((p.vis_mode == 0 ? na : min(na, kend)) + TR - 1) / TR;
-    const int ntB = p.vis_mode == 0 ? (p.b.n + TR - 1) / TR : 0;
+    const int ntB = p.vis_mode == 0 ? (nb + TR - 1) / TR : 0;
     if (t1 < 0) t1 = ntA + ntB;
+    const bool fp4a = FP4 && !xjob;          // segment A of this piece is the FP4 cache
 
     bf16x8_t qreg[D / 16];
     {
-      const uint16_t* qp = p.q + int64_t(row < p.nq ? row : 0) * p.q_row + h * D + 8 * hi;
+      const uint16_t* qp = (xjob ? p.qx : p.q) + int64_t(row < p.nq ? row : 0) * p.q_row + h * D + 8 * hi;
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
         const uint4 x = row < p.nq ? *reinterpret_cast<const uint4*>(qp + 16 * ss) : make_uint4(0, 0, 0, 0);
@@ -666,7 +696,7 @@ void attn_bf16_direct_kernel(Params p) {
     auto issue = [&](int t, uint8_t* buf) {
       const bool inA = t < ntA;
       if constexpr (FP4) {
-        if (inA) {
+        if (inA && fp4a) {
           const int r0 = t * TR;
           const int64_t e0 = h * p.a.head_stride + int64_t(r0) * p.a.row_stride;
           const int left = p.a.n - r0;
@@ -683,7 +713,7 @@ void attn_bf16_direct_kernel(Params p) {
           return;
         }
       }
-      const DevSeg& sg = inA ? p.a : p.b;
+      const DevSeg& sg = inA ? SA : p.b;
       const int r0 = (inA ? t : t - ntA) * TR;                  // first row of the tile in the segment
       const int64_t rp = sg.row_stride * 2;                      // row pitch in bytes
       const uint8_t* kb0 = sg.k + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
@@ -700,7 +730,7 @@ void attn_bf16_direct_kernel(Params p) {
     };
 
     issue(t0, smem + (t0 & 1) * DT_BUF);
-    if (FP4 && t0 < ntA) dequant_store(smem + (t0 & 1) * DT_BUF, DT_TILE, TR - 1);
+    if (fp4a && t0 < ntA) dequant_store(smem + (t0 & 1) * DT_BUF, DT_TILE, TR - 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -713,7 +743,7 @@ void attn_bf16_direct_kernel(Params p) {
 
       const bool inA = t < ntA;
       const int r0 = (inA ? t : t - ntA) * TR + u2 * BN;       // first row of the sub-tile
-      const int seg_left = (inA ? na : p.b.n) - r0;
+      const int seg_left = (inA ? na : nb) - r0;
       // a sub-tile wholly past the end is skipped (FP4: computed fully masked instead, so the
       // dequantisation below stays in one basic block with the QK products)
       if (!FP4 && seg_left <= 0) continue;
@@ -734,7 +764,7 @@ void attn_bf16_direct_kernel(Params p) {
         // FP4 (or past the piece) the stores go to a 16 KB scratch area above the two
         // buffers instead (K and V rows folded onto 64 rows), so no branch is needed
         if (u2 == SUB - 1) {
-          const bool real = t + 1 < t1 && t + 1 < ntA;
+          const bool real = fp4a && t + 1 < t1 && t + 1 < ntA;
           dequant_store(real ? smem + ((t + 1) & 1) * DT_BUF : smem + 2 * DT_BUF,
                         real ? DT_TILE : 0, real ? TR - 1 : BN - 1);
         }
@@ -845,7 +875,7 @@ void attn_bf16_direct_kernel(Params p) {
     }
     if (row < p.nq) {
       const float inv = 1.0f / l_run;
-      uint16_t* op = p.o + int64_t(row) * p.q_row + h * D + 4 * hi;
+      uint16_t* op = (xjob ? p.ox : p.o) + int64_t(row) * p.q_row + h * D + 4 * hi;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -956,6 +986,11 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
     p.n_qblk = (a.nq + DNW * 32 - 1) / (DNW * 32);
     const int blocks = p.n_qblk * a.H;
     p.n_wg = blocks;
+    const bool cross = a.qx != nullptr && a.x.n > 0;
+    if (cross && (a.vis.mode != 0 || a.x.fp4)) {
+      snprintf(err, 256, "fused cross-attention needs an unmasked call and bf16 text keys");
+      return 1;
+    }
     if (a.vis.mode == 0 && a.ws && a.n_cu > blocks && blocks <= a.ws_blocks) {
       // Split when the best main/tail cut is clearly shorter than one whole block. Cost in
       // key tiles, with kPieceCost tiles per piece for its prologue (Q load, first tile not
@@ -991,6 +1026,16 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
         p.cnt = reinterpret_cast<uint32_t*>(ws);
         p.part = reinterpret_cast<float*>(ws + split_slots_offset(a.ws_blocks));
       }
+    }
+    p.n_self_wg = p.n_wg;
+    if (cross) {
+      // cross blocks go to the CUs the self-attention leaves idle (several blocks each), or,
+      // when there are none, to one extra workgroup per block
+      const int idle = a.n_cu > p.n_self_wg ? a.n_cu - p.n_self_wg : 0;
+      p.n_wg = p.n_self_wg + (idle > 0 ? (idle < blocks ? idle : blocks) : blocks);
+      p.qx = static_cast<const uint16_t*>(a.qx);
+      p.ox = static_cast<uint16_t*>(a.ox);
+      p.x = seg(a.x);
     }
     return fp4 ? launch_direct<DNW, DSUB, true>(p, p.n_wg, s, err)
                : launch_direct<DNW, DSUB, false>(p, p.n_wg, s, err);

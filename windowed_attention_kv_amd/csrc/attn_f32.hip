@@ -116,6 +116,23 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(ParamsF p) {
 }  // namespace
 
 int launch_attention(const AttnArgs& a, void* stream, char* err) {
+  if (a.qx != nullptr && a.x.n > 0 && !(a.dtype == 1 && a.D == 128)) {
+    // no fused kernel for this shape: the self part, then the cross part as its own launch
+    AttnArgs self = a;
+    self.qx = nullptr;
+    self.ox = nullptr;
+    self.x = KeySeg{};
+    if (int r = launch_attention(self, stream, err)) return r;
+    AttnArgs cx = self;
+    cx.q = a.qx;
+    cx.o = a.ox;
+    cx.seg[0] = a.x;
+    cx.seg[1] = a.x;
+    cx.seg[1].n = 0;
+    cx.vis = Visibility{};
+    cx.ws = nullptr;
+    return launch_attention(cx, stream, err);
+  }
   if (a.dtype == 1) return launch_attention_bf16(a, stream, err);
   if (a.dtype != 0) {
     snprintf(err, 256, "dtype %d", a.dtype);

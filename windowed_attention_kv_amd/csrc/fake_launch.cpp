@@ -12,7 +12,7 @@ namespace {
 
 struct Record {
   int kind;              // 0 attention, 1 scatter, 2 quant, 3 export, 4 zero
-  int64_t f[20];
+  int64_t f[24];
 };
 
 std::vector<Record> g_log;
@@ -36,7 +36,8 @@ int launch_attention(const AttnArgs& a, void*, char* err) {
   Record r{0, {a.dtype, a.H, a.D, a.nq, a.seg[0].n, a.seg[0].fp4, a.seg[0].head_stride,
                a.seg[0].row_stride, a.seg[1].n, a.seg[1].head_stride, a.seg[1].row_stride,
                a.vis.mode, a.vis.n_sink, a.vis.base, a.vis.F, a.vis.C,
-               a.ws != nullptr, a.ws_blocks, a.ws_slots, a.n_cu}};
+               a.ws != nullptr, a.ws_blocks, a.ws_slots, a.n_cu,
+               a.qx != nullptr, a.ox != nullptr, a.x.n, a.x.row_stride}};
   g_log.push_back(r);
   return 0;
 }
@@ -85,10 +86,10 @@ void llfake_fail_next(int n) { g_fail = n; }
 
 int llfake_count(void) { return int(g_log.size()); }
 
-// kind of record i (or -1) and its 20 integer fields
+// kind of record i (or -1) and its 24 integer fields
 int llfake_record(int i, int64_t* fields) {
   if (i < 0 || i >= int(g_log.size())) return -1;
-  for (int j = 0; j < 20; ++j) fields[j] = g_log[size_t(i)].f[j];
+  for (int j = 0; j < 24; ++j) fields[j] = g_log[size_t(i)].f[j];
   return g_log[size_t(i)].kind;
 }
 

@@ -276,14 +276,28 @@ ll_status ll_cache_reset(ll_cache* cache) {
   return ok();
 }
 
-ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const void* k,
-                        const void* v, void* o, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// chunk attention, optionally with the fused text cross-attention (qx != nullptr)
+ll_status attn_chunk_impl(ll_cache* cache, int32_t layer, const void* q, const void* k,
+                          const void* v, void* o, const void* qx, const void* k_text,
+                          const void* v_text, int32_t n_text, void* ox, void* stream) {
   if (ll_status s = check_layer(cache, layer)) return s;
   if (ll_status s = check_ptr(q, "q")) return s;
   if (ll_status s = check_ptr(k, "k")) return s;
   if (ll_status s = check_ptr(v, "v")) return s;
   if (ll_status s = check_ptr(o, "o")) return s;
   const ll_cache_desc& d = cache->d;
+  if (qx) {
+    if (ll_status s = check_ptr(k_text, "k_text")) return s;
+    if (ll_status s = check_ptr(v_text, "v_text")) return s;
+    if (ll_status s = check_ptr(ox, "ox")) return s;
+    if (n_text < 1 || int64_t(n_text) * d.num_heads * d.head_dim * (d.dtype == LL_BF16 ? 2 : 4) >=
+                          (int64_t(1) << 31))
+      return fail(LL_EINVAL, "n_text %d", n_text);
+  }
   const int32_t n = d.chunk_frames * d.tokens_per_frame;
   ll::AttnArgs a;
   a.dtype = d.dtype;
@@ -308,9 +322,31 @@ ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const voi
     a.ws = ws;
     a.ws_blocks = cache->L.ws_blocks;
     a.ws_slots = cache->L.ws_slots;
-    a.n_cu = cache->n_cu;
+  }
+  a.n_cu = cache->n_cu;
+  if (qx) {
+    a.qx = qx;
+    a.ox = ox;
+    a.x = input_segment(d, k_text, v_text, n_text);
   }
   return device_status(ll::launch_attention(a, stream, msg), "attention launch", msg) ?: ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const void* k,
+                        const void* v, void* o, void* stream) {
+  return attn_chunk_impl(cache, layer, q, k, v, o, nullptr, nullptr, nullptr, 0, nullptr, stream);
+}
+
+ll_status ll_attn_chunk_cross(ll_cache* cache, int32_t layer, const void* q, const void* k,
+                              const void* v, const void* qx, const void* k_text,
+                              const void* v_text, int32_t n_text, void* o, void* ox,
+                              void* stream) {
+  if (!qx) return fail(LL_EINVAL, "qx is NULL");
+  return attn_chunk_impl(cache, layer, q, k, v, o, qx, k_text, v_text, n_text, ox, stream);
 }
 
 ll_status ll_cache_commit(ll_cache* cache, int32_t layer, const void* k, const void* v,
