@@ -10,6 +10,9 @@ only to lay out `export()`. A cross-check asserts that every committed frame a c
 is one the layer still holds, tying the visible set to the eviction rule.
 
 Readings taken:
+  * multi-shot sink ([DIST] 序列并行与注意力汇聚的协同设计): new_shot() marks the next committed
+    frame as the first of a new shot; its first S frames become the sink and the previous
+    shot's sink frames stop being visible unless they are still in the window;
   * the own chunk is attended bidirectionally and unquantised; only committed history is
     stored in FP4 (quantisation happens on commit);
   * only the last denoise step of a chunk commits (earlier steps leave no trace);
@@ -36,6 +39,7 @@ class LayerModel:
         self.scale = 1.0 / math.sqrt(D) if scale is None else scale
         self.kv_format = kv_format
         self.F = 0
+        self.B = 0           # first frame of the current shot
         self.k = {}          # frame -> stored K values [T,H,D] float64
         self.v = {}
         self.k_fp4 = {}      # frame -> (packed [T*H, D/2], scales [T*H, D/16]) under FP4
@@ -58,7 +62,11 @@ class LayerModel:
         return self.F // self.C
 
     def held(self) -> list[int]:
-        return ring.held_frames(self.F, self.S, self.W)
+        return ring.held_frames(self.F, self.S, self.W, self.B)
+
+    def new_shot(self):
+        """The next committed frame starts a new shot (multi-shot sink)."""
+        self.B = self.F
 
     # -- chunk attention -----------------------------------------------------------------
     def keys_for_chunk(self, k_own, v_own):
@@ -66,7 +74,7 @@ class LayerModel:
         s = self.F
         held = set(self.held())
         ks, vs, fr = [], [], []
-        for f in ring.visible_frames(self.chunk, self.C, self.S, self.W):
+        for f in ring.visible_frames(self.chunk, self.C, self.S, self.W, self.B):
             if f < s:
                 assert f in held, f"chunk {self.chunk} sees frame {f} that was evicted"
                 ks.append(self.k[f])
@@ -127,7 +135,7 @@ class LayerModel:
 
     # -- inspection ------------------------------------------------------------------------
     def slot_map(self) -> list[int]:
-        return ring.slot_map(self.F, self.S, self.W)
+        return ring.slot_map(self.F, self.S, self.W, self.B)
 
     def export_dense(self):
         """Slot-order K, V [(S+W)*T, H, D]; empty slots are NaN."""
@@ -158,15 +166,17 @@ class LayerModel:
 
 
 def bruteforce_chunk(q, hist_k, hist_v, chunk: int, C: int, S: int, W: int, T: int,
-                     scale: float, rows=None) -> np.ndarray:
+                     scale: float, rows=None, shot_start: int = 0) -> np.ndarray:
     """Chunk attention over the WHOLE history (every frame ever produced, own chunk
     included, frame-major [n_frames*T, H, D]) with an explicit frame mask: key frame fk is
-    visible to the chunk iff it is a sink frame, one of the W frames before the chunk, or
-    in the chunk. Nothing is evicted; masked keys contribute exactly zero."""
+    visible to the chunk iff it is a sink frame of the chunk's shot (the shot's first S
+    frames), one of the W frames before the chunk, or in the chunk. Nothing is evicted;
+    masked keys contribute exactly zero."""
     s = chunk * C
     n_frames = np.asarray(hist_k).shape[0] // T
     fk = np.arange(n_frames)
-    vis = (fk < S) | ((fk >= s - W) & (fk < s)) | ((fk >= s) & (fk < s + C))
+    B = shot_start
+    vis = ((fk >= B) & (fk < B + S)) | ((fk >= s - W) & (fk < s)) | ((fk >= s) & (fk < s + C))
     vis &= fk < s + C
     key_vis = np.repeat(vis, T)
 

@@ -75,6 +75,55 @@ def test_first_chunk_is_plain_attention():
     assert np.max(np.abs(o - ref)) <= 1e-12
 
 
+@pytest.mark.parametrize("shots", [(2,), (5,), (1, 2), (4, 9)])
+def test_multi_shot_cache_path_vs_bruteforce(shots):
+    """Multi-shot sink: new_shot() before the chunks in `shots`; every chunk matches brute
+    force over the whole history with the sink taken from the chunk's own shot."""
+    shape = SMALL_LAYER
+    C = shape.chunk_frames
+    m = _model(shape)
+    chunks = _stream(shape, shape.chunks)
+    hist_k, hist_v = [], []
+    scale = 1 / math.sqrt(shape.head_dim)
+    B = 0
+    for c, (q, k, v) in enumerate(chunks):
+        if c in shots:
+            m.new_shot()
+            B = c * C
+        o = m.attn_chunk(q.values, k.values, v.values)
+        hk = np.concatenate(hist_k + [k.values]).astype(np.float64)
+        hv = np.concatenate(hist_v + [v.values]).astype(np.float64)
+        ref = bruteforce_chunk(q.values, hk, hv, c, C, shape.sink_frames, shape.window_frames,
+                               shape.tokens_per_frame, scale, shot_start=B)
+        assert np.max(np.abs(o - ref)) <= 1e-12, c
+        m.commit(k.values, v.values)
+        hist_k.append(k.values)
+        hist_v.append(v.values)
+
+
+def test_new_shot_drops_the_old_sink():
+    """After a shot boundary the old shot's sink frames stop mattering once they are out of
+    the window, and the new shot's first chunk matters for every later chunk of the shot."""
+    shape = synth.CONFIGS["tiny"]          # S = 3, W = 6, C = 3
+    chunks = _stream(shape, 12)
+    m1, m2, m3 = _model(shape), _model(shape), _model(shape)
+    for c, (q, k, v) in enumerate(chunks):
+        if c == 4:
+            for m in (m1, m2, m3):
+                m.new_shot()
+        if c >= 4:
+            a = m1.attn_chunk(q.values, k.values, v.values)
+            b = m2.attn_chunk(q.values, k.values, v.values)
+            np.testing.assert_array_equal(a, b)       # old sink (chunk 0) is gone
+        if c >= 5:
+            d = m3.attn_chunk(q.values, k.values, v.values)
+            assert np.max(np.abs(a - d)) > 1e-3, c    # the new sink (chunk 4) is seen
+        for m, kk, vv in ((m1, k.values, v.values),
+                          (m2, k.values * (1.5 if c == 0 else 1.0), v.values + (1.0 if c == 0 else 0.0)),
+                          (m3, k.values * (1.5 if c == 4 else 1.0), v.values + (1.0 if c == 4 else 0.0))):
+            m.commit(kk, vv)
+
+
 def test_evicted_frames_have_no_influence():
     """I3: the outputs do not change, bit for bit, when evicted frames are perturbed
     (cache path: poisoned with NaN; brute force: replaced by large finite values)."""
@@ -160,7 +209,7 @@ def test_recache_equals_streaming_from_scratch(n_chunks):
     # frame ids and slots unchanged, values replaced
     K, _ = m.export_dense()
     for i, f in enumerate(frames):
-        slot = ring.slot_of_frame(f, shape.sink_frames, shape.window_frames)
+        slot = ring.slot_of_frame(f, m.F, shape.sink_frames, shape.window_frames)
         T = shape.tokens_per_frame
         np.testing.assert_array_equal(K[slot * T:(slot + 1) * T], k.values[i * T:(i + 1) * T])
 

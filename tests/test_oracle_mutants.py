@@ -16,18 +16,23 @@ import test_oracle_ring as t_ring
 from windowed_attention_kv_amd import synth
 
 
-def _window_one_longer(chunk, C, S, W):
+def _window_one_longer(chunk, C, S, W, shot_start=0):
     s = chunk * C
-    return sorted(set(range(min(S, s + C))) | set(range(max(0, s - W - 1), s)) | set(range(s, s + C)))
+    return sorted(set(range(shot_start, min(shot_start + S, s + C)))
+                  | set(range(max(0, s - W - 1), s)) | set(range(s, s + C)))
 
 
-def _sink_dropped(chunk, C, S, W):
+def _sink_dropped(chunk, C, S, W, shot_start=0):
     s = chunk * C
     return sorted(set(range(max(0, s - W), s)) | set(range(s, s + C)))
 
 
-def _slot_wrong(f, S, W):
-    return f if f < S else S + (f % W)
+def _slot_wrong(f, F, S, W, shot_start=0):
+    return (f + 1) % W if f >= F - W else W + (f - shot_start)
+
+
+def _spill_late(F, S, W, shot_start=0):
+    return min(max(F - W - shot_start - 1, 0), S)
 
 
 def _ties_to_odd(y):
@@ -64,7 +69,9 @@ MUTANTS = [
     ("sink dropped", ring_mod, "visible_frames", _sink_dropped,
      lambda: t_model.test_cache_path_vs_bruteforce(synth.CONFIGS["tiny"])),
     ("slot formula", ring_mod, "slot_of_frame", _slot_wrong,
-     lambda: t_ring.test_ring_vs_fifo(3, 9, 3)),
+     lambda: t_ring.test_ring_vs_simulation_single_shot(3, 9, 3)),
+    ("sink spill one frame late", ring_mod, "n_spilled", _spill_late,
+     lambda: t_ring.test_ring_vs_simulation_multi_shot(3, 9, 3)),
     ("fp4 ties to odd", fp4_mod, "encode_magnitude", _ties_to_odd,
      t_fp4.test_exhaustive_vs_brute_force),
     ("fp4 scale off by one", fp4_mod, "scale_bytes", _scale_off_by_one,

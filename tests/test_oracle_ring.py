@@ -1,5 +1,6 @@
-"""Pins for oracle/ring.py: the slot map and held frames against a FIFO simulation, and
-the visible-frame set against the eviction rule."""
+"""Pins for oracle/ring.py: the slot map and held frames against a frame-by-frame slot
+simulation (single shot and multi-shot), and the visible-frame set against the eviction
+rule."""
 import collections
 
 import pytest
@@ -7,44 +8,70 @@ import pytest
 from oracle import ring
 
 
-def fifo_simulation(n_frames, C, S, W):
-    """Frame-by-frame cache simulation with an explicit FIFO of window frames: sink frames
-    get slots 0..S-1 in arrival order; a window frame takes the next free window slot or,
-    when the window is full, the slot of the frame it pushes out of the FIFO."""
-    sink = []
+def slot_simulation(n_frames, C, S, W, shot_starts=()):
+    """Frame-by-frame cache with explicit slot lists. Window slots 0..W-1 are handed out in
+    order and then reused by FIFO: a frame takes the slot of the frame it pushes out of the
+    window. A pushed-out frame that is one of the current shot's first S frames moves to sink
+    slot W + (its index in the shot). A new shot (at a frame in `shot_starts`) forgets the
+    previous shot's sink frames. Yields (frames committed, slot -> frame, held frames) at
+    every chunk boundary."""
     fifo = collections.deque()
     slot_of = {}
-    free = list(range(S, S + W))
+    sink = {}
+    free = list(range(W))
+    shot = 0
     snapshots = []
     for f in range(n_frames):
-        if len(sink) < S:
-            slot_of[f] = len(sink)
-            sink.append(f)
+        if f in shot_starts:
+            shot = f
+            sink = {}
+        if len(fifo) == W:
+            old = fifo.popleft()
+            slot = slot_of.pop(old)
+            if shot <= old < shot + S:
+                sink[old] = W + (old - shot)
         else:
-            if len(fifo) == W:
-                old = fifo.popleft()
-                slot = slot_of.pop(old)
-            else:
-                slot = free.pop(0)
-            slot_of[f] = slot
-            fifo.append(f)
+            slot = free.pop(0)
+        slot_of[f] = slot
+        fifo.append(f)
         if (f + 1) % C == 0:
+            F = f + 1
+            if F in shot_starts:        # a shot starting at the next frame is already open
+                shot_now, sink_now = F, {}
+            else:
+                shot_now, sink_now = shot, sink
             slots = [-1] * (S + W)
-            for fr, sl in slot_of.items():
+            for fr, sl in list(slot_of.items()) + list(sink_now.items()):
                 slots[sl] = fr
-            snapshots.append((f + 1, slots, sorted(sink + list(fifo))))
+            snapshots.append((F, shot_now, slots, sorted(list(fifo) + list(sink_now))))
     return snapshots
 
 
 @pytest.mark.parametrize("S", range(0, 5))
 @pytest.mark.parametrize("W", range(1, 13))
 @pytest.mark.parametrize("C", range(1, 5))
-def test_ring_vs_fifo(S, W, C):
+def test_ring_vs_simulation_single_shot(S, W, C):
     n = 600 if (S + W) < 8 else 300
-    for F, slots, held in fifo_simulation(n * C, C, S, W):
+    for F, B, slots, held in slot_simulation(n * C, C, S, W):
+        assert B == 0
         assert ring.slot_map(F, S, W) == slots
         assert ring.held_frames(F, S, W) == held
         nv = ring.valid_slots(F, S, W)
+        assert nv == len(held)
+        assert all(x >= 0 for x in slots[:nv]) and all(x < 0 for x in slots[nv:])
+
+
+@pytest.mark.parametrize("S", range(0, 5))
+@pytest.mark.parametrize("W", range(1, 11))
+@pytest.mark.parametrize("C", range(1, 4))
+def test_ring_vs_simulation_multi_shot(S, W, C):
+    # shots of 1, 2, 5 and 17 chunks, and two boundaries in a row
+    starts = {c * C for c in (1, 3, 8, 25, 26, 40)}
+    for F, B, slots, held in slot_simulation(60 * C, C, S, W, starts):
+        assert ring.slot_map(F, S, W, B) == slots, (F, B)
+        assert ring.held_frames(F, S, W, B) == held
+        nv = ring.valid_slots(F, S, W, B)
+        assert nv == len(held)
         assert all(x >= 0 for x in slots[:nv]) and all(x < 0 for x in slots[nv:])
 
 
@@ -60,14 +87,18 @@ def test_long_stream_constant_memory():
 
 
 @pytest.mark.parametrize("S,W,C", [(3, 6, 3), (3, 9, 3), (2, 5, 3), (0, 4, 2), (4, 3, 1)])
-def test_visible_committed_frames_are_exactly_the_held_frames(S, W, C):
+@pytest.mark.parametrize("shot_chunk", [None, 1, 4, 7])
+def test_visible_committed_frames_are_exactly_the_held_frames(S, W, C, shot_chunk):
+    B = 0
     for c in range(40):
         s = c * C
-        vis = ring.visible_frames(c, C, S, W)
+        if shot_chunk is not None and c == shot_chunk:
+            B = s
+        vis = ring.visible_frames(c, C, S, W, B)
         assert vis == sorted(set(vis))
         assert [f for f in vis if f >= s] == list(range(s, s + C))
         committed = [f for f in vis if f < s]
-        assert committed == ring.held_frames(s, S, W)
+        assert committed == ring.held_frames(s, S, W, B)
 
 
 def test_visible_counts_layer_config():
@@ -77,3 +108,17 @@ def test_visible_counts_layer_config():
     # tiny: 16-token frames, chunk 3, sink 3, window 6: 3, 6, 9, 12, 12, ...
     counts = [len(ring.visible_frames(c, 3, 3, 6)) for c in range(8)]
     assert counts == [3, 6, 9, 12, 12, 12, 12, 12]
+
+
+def test_new_shot_resets_the_sink():
+    """Layer config, shot boundary at chunk 10 (frame 30): the first chunk of the new shot
+    sees only the window (frames 21..29) and itself; three chunks later the new shot's first
+    chunk is its sink and the old sink frames 0..2 are gone."""
+    C, S, W = 3, 3, 9
+    assert ring.visible_frames(10, C, S, W, 0) == [0, 1, 2] + list(range(21, 33))
+    assert ring.visible_frames(10, C, S, W, 30) == list(range(21, 33))
+    assert ring.visible_frames(11, C, S, W, 30) == list(range(24, 36))
+    assert ring.visible_frames(14, C, S, W, 30) == [30, 31, 32] + list(range(33, 45))
+    assert ring.held_frames(42, S, W, 30) == [30, 31, 32] + list(range(33, 42))
+    # the old shot's sink is still visible while inside the window of a short shot
+    assert ring.visible_frames(2, C, S, W, 3) == list(range(0, 9))
