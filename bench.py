@@ -296,6 +296,35 @@ def commit_batch_row(torch, shape, Cache, kv_format, k, v):
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def spill_commit_row(torch, shape, Cache, k, v):
+    """The commit that retires a shot's sink frames from the window (multi-shot sink): with
+    S = C = 3 and W = 9, the fourth commit after a shot boundary also moves the shot's first 3
+    frames from their window slots to the sink slots. Per-commit time of 30 such commits (one
+    per layer); bytes = the plain commit's plus the moved frames read and written."""
+    L = 30
+    n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
+    C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
+    cache = Cache(L, H, D, T, C, S, W)
+    tm = EventTimer(torch)
+    for rep in range(11):
+        for layer in range(L):
+            cache.new_shot(layer)
+            for _ in range(W // C):
+                cache.commit(layer, k, v)
+        s = tm.start()
+        for layer in range(L):
+            cache.commit(layer, k, v)
+        tm.stop(s, "spill" if rep else "warm")
+    torch.cuda.synchronize()
+    ms = tm.totals()["spill"][0] / (10 * L)
+    moved = 2 * 2 * S * T * H * D * 2
+    nbytes = 2 * 2 * n * H * D * 2 + moved
+    gbs = nbytes / ms / 1e6
+    return {"us_per_commit": round(ms * 1e3, 3), "bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "note": f"commit that moves {S} sink frames (K and V) to the sink slots"}
+
+
 def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     """Commit batches, FP4 stream, standalone quant, recache and the 30-layer stacks."""
     res = {}
@@ -304,6 +333,7 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
     res["commit_30_layers"] = commit_batch_row(torch, shape, Cache, "dense", inputs[0][1], inputs[0][2])
     res["fp4_commit_30_layers"] = commit_batch_row(torch, shape, Cache, "fp4", inputs[0][1], inputs[0][2])
+    res["spill_commit_30_layers"] = spill_commit_row(torch, shape, Cache, inputs[0][1], inputs[0][2])
     # FP4 KV store at the layer shape: steady-state attention (15 visible frames)
     c4 = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
                shape.window_frames, kv_format="fp4")

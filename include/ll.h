@@ -67,7 +67,7 @@ typedef struct {
   int32_t num_heads;       /* H >= 1 */
   int32_t head_dim;        /* D: 64 or 128 */
   int32_t tokens_per_frame;/* T >= 1 */
-  int32_t chunk_frames;    /* C >= 1: frames produced (and committed) per chunk */
+  int32_t chunk_frames;    /* C >= 1: frames produced (and committed) per chunk; C <= W */
   int32_t sink_frames;     /* S >= 0: frames 0..S-1 are pinned for good ("sink_size") */
   int32_t window_frames;   /* W >= 1: committed frames kept before the chunk ("local_attn_size") */
   int32_t dtype;           /* ll_dtype of Q/K/V/O and of the dense cache */
@@ -96,8 +96,17 @@ ll_status ll_cache_create(const ll_cache_desc* desc, void* device_mem, size_t de
 /* Free the handle (not the device memory). NULL is accepted. */
 ll_status ll_cache_destroy(ll_cache* cache);
 
-/* Mark every layer empty (host metadata only). */
+/* Mark every layer empty and back at the first shot (host metadata only). */
 ll_status ll_cache_reset(ll_cache* cache);
+
+/* Shot boundary of a multi-shot video for `layer` ("LongLive 2.0" distributed-inference
+ * page, section on sequence parallelism and the attention sink: the multi-shot sink is reset
+ * at every shot boundary). The next committed frame starts a new shot: from now on the sink
+ * is that shot's first S frames, the previous shot's sink frames stop being visible (unless
+ * they are still among the last W committed frames), and the window is unchanged. Host
+ * metadata only; nothing moves. Call it for every layer at the boundary. LL_EINVAL for a bad
+ * handle or layer. */
+ll_status ll_cache_new_shot(ll_cache* cache, int32_t layer);
 
 /* Window+sink chunk attention for the next chunk of `layer` (chunk index = frames
  * committed / C). q, k, v, o: [C*T, H, D]. For each head and query row:
@@ -128,9 +137,11 @@ ll_status ll_attn_chunk_cross(ll_cache* cache, int32_t layer, const void* q, con
                               void* stream);
 
 /* Append the chunk's K/V ([C*T, H, D], the final denoise step's values) as frames
- * F..F+C-1 (F = frames committed) and advance F by C. Frame f goes to slot f if f < S and
- * to slot S + (f-S) mod W otherwise; writing a window slot evicts the frame W earlier. One
- * fused launch writes K and V (bit copies, or FP4 quantisation under LL_KV_FP4). */
+ * F..F+C-1 (F = frames committed) and advance F by C. Slots 0..W-1 are the window, W..W+S-1
+ * the sink: frame f goes to window slot f mod W, evicting frame f-W; an evicted frame that is
+ * one of the current shot's first S frames (first frame B) is moved to sink slot W + (f-W-B)
+ * in the same launch. One fused launch writes K and V (bit copies, or FP4 quantisation
+ * under LL_KV_FP4; moved sink frames keep their bytes). */
 ll_status ll_cache_commit(ll_cache* cache, int32_t layer, const void* k, const void* v,
                           void* stream);
 

@@ -76,34 +76,62 @@ def _state(f, h, layer, slots):
 
 def _kernel_slot(rec, r):
     """Destination slot of source frame rank r as the scatter kernel computes it (launch.h)."""
-    n_frames, n_lead, lead0, S, W, first_ring = rec[5], rec[6], rec[7], rec[8], rec[9], rec[10]
+    n_frames, n_lead, lead0, ring_base, W, first_ring = rec[5], rec[6], rec[7], rec[8], rec[9], rec[10]
     if r < n_lead:
         return lead0 + r
-    return S + (first_ring + r - n_lead) % W
+    return ring_base + (first_ring + r - n_lead) % W
 
 
-@pytest.mark.parametrize("S,W,C", [(3, 6, 3), (3, 9, 3), (2, 5, 3), (0, 4, 2), (4, 3, 1), (5, 2, 3)])
-def test_commit_slots_and_state_follow_the_ring(fake, S, W, C):
+def _apply_scatter(slots, rec, frames):
+    """Move frame ids through a slot list the way the scatter kernel moves data: rank r's
+    destination is first copied to its spill slot (when r is in the spill range), then
+    overwritten with frame frames[r]."""
+    lo, hi, sp0 = rec[12], rec[13], rec[14]
+    for r in range(rec[5]):
+        dst = _kernel_slot(rec, r)
+        if lo <= r < hi:
+            slots[sp0 + (r - lo)] = slots[dst]
+        slots[dst] = frames[r]
+
+
+@pytest.mark.parametrize("S,W,C", [(3, 6, 3), (3, 9, 3), (2, 5, 3), (0, 4, 2), (4, 3, 1), (5, 3, 3),
+                                   (1, 1, 1)])
+@pytest.mark.parametrize("shots", [(), (4,), (2, 3, 11), (1, 9, 10, 17)])
+def test_commit_slots_and_state_follow_the_ring(fake, S, W, C, shots):
+    """Stream 25 chunks (new shots before the chunks in `shots`); replay every commit's
+    scatter arguments on a slot -> frame list: the held slots must hold exactly the oracle's
+    slot map, attention must read exactly the held prefix, and ll_cache_state must agree."""
     h, _ = _create(fake, sink_frames=S, window_frames=W, chunk_frames=C)
+    sim = [-1] * (S + W)
+    B = 0
     for chunk in range(25):
         F = chunk * C
+        if chunk in shots:
+            assert fake.ll_cache_new_shot(h, 1) == 0
+            B = F
         fake.llfake_reset()
         assert fake.ll_attn_chunk(h, 1, P, P, P, P, None) == 0
         assert fake.ll_cache_commit(h, 1, P, P, None) == 0
         (ka, att), (kc, com) = _records(fake)
         assert ka == 0 and kc == 1
         # attention reads exactly the held frames' slots (a prefix) plus the own chunk
-        assert att[4] == ring.valid_slots(F, S, W) * 16
+        assert att[4] == ring.valid_slots(F, S, W, B) * 16
         assert att[8] == C * 16 and att[11] == 0
-        # the commit writes frame F+i into ring.slot_of_frame(F+i)
         assert com[5] == C
-        for i in range(C):
-            assert _kernel_slot(com, i) == ring.slot_of_frame(F + i, S, W)
-        Fs, slots = _state(fake, h, 1, S + W)
-        assert Fs == F + C and slots == ring.slot_map(F + C, S, W)
+        _apply_scatter(sim, com, list(range(F, F + C)))
+        want = ring.slot_map(F + C, S, W, B)
+        assert [x if want[i] >= 0 else -1 for i, x in enumerate(sim)] == want
+        assert _state(fake, h, 1, S + W) == (F + C, want)
         # layer 0 untouched
         assert _state(fake, h, 0, S + W) == (0, [-1] * (S + W))
     fake.ll_cache_destroy(h)
+
+
+def test_window_shorter_than_a_chunk_is_rejected(fake):
+    d = make_desc(1, 2, 64, 16, 3, 5, 2, dtype="f32")
+    size = ctypes.c_size_t()
+    assert fake.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == _lib.LL_EUNSUPPORTED
+    assert b"window_frames" in fake.ll_last_error()
 
 
 @pytest.mark.parametrize("chunks", [1, 2, 3, 4, 5, 9])
@@ -113,43 +141,75 @@ def test_recache_launches(fake, chunks):
     for _ in range(chunks):
         assert fake.ll_cache_commit(h, 0, P, P, None) == 0
     F = chunks * C
-    held = ring.held_frames(F, S, W)
+    held = ring.held_frames(F, S, W, 0)
     fake.llfake_reset()
     assert fake.ll_recache(h, 0, P, P, P, P, P, P, 512, P, P, None) == 0
     recs = _records(fake)
     assert [k for k, _ in recs] == [0, 0, 1]
     self_att, cross, rewrite = recs[0][1], recs[1][1], recs[2][1]
     assert self_att[3] == len(held) * T and self_att[4] == len(held) * T and self_att[11] == 1
-    assert self_att[12] == min(F, S) and self_att[13] == max(S, F - W) and self_att[14] == F
+    assert self_att[12] == ring.n_spilled(F, S, W) and self_att[13] == max(0, F - W)
+    assert self_att[14] == F and self_att[15] == 0
     assert cross[3] == len(held) * T and cross[4] == 512 and cross[11] == 0
     assert rewrite[5] == len(held)
+    assert rewrite[12] == rewrite[13]          # no spill
     for r, f in enumerate(held):
-        assert _kernel_slot(rewrite, r) == ring.slot_of_frame(f, S, W)
+        assert _kernel_slot(rewrite, r) == ring.slot_of_frame(f, F, S, W)
     # the recache keeps frame ids and slots
     assert _state(fake, h, 0, S + W) == (F, ring.slot_map(F, S, W))
     fake.ll_cache_destroy(h)
 
 
-def _limit_closed_form(row, T, C, n_sink, base, F):
+def _limit_closed_form(row, T, C, n_sink, base, F, sink0):
     """The kernels' per-row key limit (launch.h Visibility mode 1)."""
     r = row // T
-    f = r if r < n_sink else base + (r - n_sink)
+    f = sink0 + r if r < n_sink else base + (r - n_sink)
     X = (f // C + 1) * C
-    return T * (min(n_sink, X) + max(0, min(F, X) - base))
+    return T * (min(max(X - sink0, 0), n_sink) + max(0, min(F, X) - base))
 
 
-@pytest.mark.parametrize("S,W,C,chunks", [(3, 9, 3, 10), (3, 9, 3, 2), (2, 5, 3, 7), (4, 6, 2, 9)])
-def test_recache_key_limit_matches_block_causal_mask(S, W, C, chunks):
+@pytest.mark.parametrize("S,W,C,chunks,shot", [(3, 9, 3, 10, 0), (3, 9, 3, 2, 0), (2, 5, 3, 7, 0),
+                                               (4, 6, 2, 9, 0), (3, 9, 3, 10, 3), (3, 6, 3, 9, 4),
+                                               (4, 6, 2, 12, 7), (2, 5, 3, 9, 8)])
+def test_recache_key_limit_matches_block_causal_mask(S, W, C, chunks, shot):
+    """The closed-form key limit the host hands the kernels equals the oracle's block-causal
+    mask over the held frames (single shot, and a shot started `shot` chunks in)."""
     from oracle.model import LayerModel
     T = 4
     F = chunks * C
     m = LayerModel(S, W, C, T, 1, 16)
+    m.F = shot * C
+    m.new_shot()
     m.F = F
     frames = m.held()
     mask = m.recache_mask(frames)(range(len(frames) * T))
+    B = shot * C
     for row in range(len(frames) * T):
-        lim = _limit_closed_form(row, T, C, min(F, S), max(S, F - W), F)
+        lim = _limit_closed_form(row, T, C, ring.n_spilled(F, S, W, B), max(0, F - W), F, B)
         assert list(mask[row]) == [j < lim for j in range(len(frames) * T)]
+
+
+def test_recache_after_a_new_shot(fake):
+    """Held frames after a shot boundary: the spilled sink frames of the new shot first
+    (sink slots), then the window; the rewrite puts every frame back in its slot."""
+    S, W, C, T = 3, 6, 3, 16
+    h, _ = _create(fake, sink_frames=S, window_frames=W, chunk_frames=C, dtype="bf16")
+    for chunk in range(9):
+        if chunk == 4:
+            assert fake.ll_cache_new_shot(h, 0) == 0
+        assert fake.ll_cache_commit(h, 0, P, P, None) == 0
+    F, B = 27, 12
+    held = ring.held_frames(F, S, W, B)
+    assert held == [12, 13, 14] + list(range(21, 27))
+    fake.llfake_reset()
+    assert fake.ll_recache(h, 0, P, P, P, P, P, P, 64, P, P, None) == 0
+    self_att, cross, rewrite = (f for _, f in _records(fake))
+    assert self_att[3] == len(held) * T and self_att[12:16] == [3, 21, 27, 12]
+    for r, f in enumerate(held):
+        assert _kernel_slot(rewrite, r) == ring.slot_of_frame(f, F, S, W, B)
+    assert _state(fake, h, 0, S + W) == (F, ring.slot_map(F, S, W, B))
+    assert fake.ll_cache_new_shot(h, 5) == _lib.LL_EINVAL
+    fake.ll_cache_destroy(h)
 
 
 def test_errors_leave_state_unchanged(fake):

@@ -48,17 +48,22 @@ def _check_export(cache, model, shape, layer=0):
         valid = ~np.isnan(MK[:, 0, 0])
         np.testing.assert_array_equal(K[valid], MK[valid])
         np.testing.assert_array_equal(V[valid], MV[valid])
-        assert valid.sum() == ring.valid_slots(model.F, shape.sink_frames, shape.window_frames) * T
+        assert valid.sum() == ring.valid_slots(model.F, shape.sink_frames, shape.window_frames,
+                                               model.B) * T
 
 
 def run_stream(shape, n_chunks, kv_format="dense", compare=None, rows=None, steps=1,
-               export_every=True, **kw):
+               export_every=True, shots=(), **kw):
     """Stream n_chunks through the library and the oracle; compare the chunks in `compare`
-    (default all) on `rows` (default all) for every denoise step."""
+    (default all) on `rows` (default all) for every denoise step. A new shot starts before
+    each chunk in `shots`."""
     cache = _cache(shape, kv_format)
     model = _model(shape, kv_format)
     worst = (0.0, 0.0)
     for c in range(n_chunks):
+        if c in shots:
+            cache.new_shot()
+            model.new_shot()
         for step in range(steps):
             q, k, v = synth.chunk_inputs(shape, 0, step, c, **kw)
             tq, tk, tv = q.torch("cuda"), k.torch("cuda"), v.torch("cuda")
@@ -370,4 +375,44 @@ def test_attn_chunk_cross_layer_config_sampled():
     shape = synth.CONFIGS["layer"]
     log("case: fused cross-attention, layer config, sampled rows")
     _cross_stream(shape, 6, 512, compare={0, 5}, rows=sample_rows(shape.n_query, 48, seed=5))
+
+
+@pytest.mark.parametrize("kind", ["bf16-d128", "bf16-d64", "fp32", "fp4"])
+def test_multi_shot_stream(kind):
+    """Multi-shot sink: new shots before chunks 3, 4 and 9 of a 14-chunk stream. Every chunk
+    matches the oracle and every export is bit-exact, so each sink frame's move from its
+    window slot to its sink slot (and the old sink's retirement) is checked."""
+    base = synth.CONFIGS["tiny"] if kind == "fp32" else synth.shrink(
+        synth.CONFIGS["layer"], heads=2, tokens_per_frame=48,
+        head_dim=64 if kind == "bf16-d64" else 128)
+    shape = synth.shrink(base, name=f"shots-{kind}")
+    log(f"case: multi-shot stream, {kind}")
+    run_stream(shape, 14, kv_format="fp4" if kind == "fp4" else "dense", shots=(3, 4, 9))
+
+
+def test_recache_after_a_new_shot():
+    """A prompt switch after a shot boundary: recache over the new shot's sink frames and the
+    window (block-causal by chunk), then more chunks of the shot."""
+    shape = synth.shrink(synth.CONFIGS["layer"], name="shot-recache", heads=2, tokens_per_frame=64)
+    log("case: recache after a new shot")
+    cache, model = run_stream(shape, 12, compare=set(), export_every=False, shots=(5,))
+    n = len(model.held()) * shape.tokens_per_frame
+    assert model.held() == [15, 16, 17] + list(range(27, 36))
+    ins = synth.recache_inputs(shape, 0, n, 33)
+    q, k, v, qx, kt, vt = ins
+    o, ox = cache.recache(0, *(t.torch("cuda") for t in ins))
+    ref_o, ref_ox = model.recache(q.values, k.values, v.values, qx.values, kt.values, vt.values,
+                                  k.bits, v.bits)
+    assert_close(to_np(o), ref_o, "bf16", "recache self after a new shot")
+    assert_close(to_np(ox), ref_ox, "bf16", "recache cross after a new shot")
+    _check_export(cache, model, shape)
+    for c in range(12, 15):
+        qq, kk, vv = synth.chunk_inputs(shape, 0, 0, c, salt=9)
+        tk, tv = kk.torch("cuda"), vv.torch("cuda")
+        oo = cache.attn_chunk(0, qq.torch("cuda"), tk, tv)
+        assert_close(to_np(oo), model.attn_chunk(qq.values, kk.values, vv.values), "bf16",
+                     f"after recache chunk {c}")
+        cache.commit(0, tk, tv)
+        model.commit(kk.values, vv.values, kk.bits, vv.bits)
+        _check_export(cache, model, shape)
 

@@ -119,6 +119,13 @@ class Cache:
         check(self._lib, self._lib.ll_cache_commit(self.handle, layer, self._check(k, n, "k"),
                                                    self._check(v, n, "v"), _stream(self.device)))
 
+    def new_shot(self, layer=None):
+        """Shot boundary (multi-shot sink): the next committed frame of `layer` (default:
+        every layer) starts a new shot whose first S frames become the sink."""
+        layers = range(self.layers) if layer is None else [layer]
+        for l in layers:
+            check(self._lib, self._lib.ll_cache_new_shot(self.handle, l))
+
     def held_rows(self, layer) -> int:
         F, slots = self.state(layer)
         return sum(1 for f in slots if f >= 0) * self.T

@@ -17,7 +17,7 @@ STATUS_NAMES = {0: "LL_OK", 1: "LL_EINVAL", 2: "LL_ESTATE", 3: "LL_EUNSUPPORTED"
 
 # every symbol include/ll.h declares
 SYMBOLS = ["ll_cache_size", "ll_cache_create", "ll_cache_destroy", "ll_cache_reset",
-           "ll_attn_chunk", "ll_attn_chunk_cross", "ll_cache_commit", "ll_recache", "ll_kv_quant",
+           "ll_cache_new_shot", "ll_attn_chunk", "ll_attn_chunk_cross", "ll_cache_commit", "ll_recache", "ll_kv_quant",
            "ll_cache_state", "ll_cache_export", "ll_last_error"]
 
 
@@ -51,6 +51,7 @@ def _declare(lib):
     lib.ll_cache_create.argtypes = [ctypes.POINTER(CacheDesc), _P, ctypes.c_size_t, ctypes.POINTER(_P)]
     lib.ll_cache_destroy.argtypes = [_P]
     lib.ll_cache_reset.argtypes = [_P]
+    lib.ll_cache_new_shot.argtypes = [_P, _I32]
     lib.ll_attn_chunk.argtypes = [_P, _I32, _P, _P, _P, _P, _P]
     lib.ll_attn_chunk_cross.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]
     lib.ll_cache_commit.argtypes = [_P, _I32, _P, _P, _P]

@@ -61,7 +61,7 @@ struct Params {
   int64_t q_row;     // elements between query rows (H * D)
   int32_t H, nq, n_qblk, n_wg;
   DevSeg a, b;
-  int32_t vis_mode, vT, vC, v_nsink, v_base, v_F;
+  int32_t vis_mode, vT, vC, v_nsink, v_base, v_F, v_sink0;
   float c;           // softmax scale * log2(e)
   // split mode (direct kernel): nt key tiles per block, the first `main` of them on the
   // block's own workgroup, the rest spread over the n_self_wg - H * n_qblk spare workgroups
@@ -86,9 +86,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ int32_t row_limit(const Params& p, int32_t row) {
   if (p.vis_mode == 0) return p.a.n + p.b.n;
   const int32_t r = row / p.vT;
-  const int32_t f = r < p.v_nsink ? r : p.v_base + (r - p.v_nsink);
+  const int32_t f = r < p.v_nsink ? p.v_sink0 + r : p.v_base + (r - p.v_nsink);
   const int32_t X = (f / p.vC + 1) * p.vC;
-  const int32_t ns = X < p.v_nsink ? X : p.v_nsink;
+  const int32_t xs = X - p.v_sink0;
+  const int32_t ns = xs < 0 ? 0 : (xs < p.v_nsink ? xs : p.v_nsink);
   const int32_t top = X < p.v_F ? X : p.v_F;
   const int32_t nr = top > p.v_base ? top - p.v_base : 0;
   return (ns + nr) * p.vT;
@@ -967,6 +968,7 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
   p.v_nsink = a.vis.n_sink;
   p.v_base = int32_t(a.vis.base);
   p.v_F = int32_t(a.vis.F);
+  p.v_sink0 = int32_t(a.vis.sink0);
   p.c = a.scale * 1.4426950408889634f;
   if (a.nq <= 0) return 0;
   if (p.a.n + p.b.n <= 0) {

@@ -35,7 +35,7 @@ struct ParamsF {
   int32_t nq, n_qblk;
   SegF a, b;
   int32_t vis_mode, vT, vC, v_nsink;
-  int64_t v_base, v_F;
+  int64_t v_base, v_F, v_sink0;
   float scale;
 };
 
@@ -43,9 +43,10 @@ __device__ int32_t row_limit_f(const ParamsF& p, int32_t row) {
   const int32_t total = p.a.n + p.b.n;
   if (p.vis_mode == 0) return total;
   const int32_t r = row / p.vT;
-  const int64_t f = r < p.v_nsink ? int64_t(r) : p.v_base + (r - p.v_nsink);
+  const int64_t f = r < p.v_nsink ? p.v_sink0 + r : p.v_base + (r - p.v_nsink);
   const int64_t X = (f / p.vC + 1) * p.vC;
-  const int64_t ns = X < p.v_nsink ? X : int64_t(p.v_nsink);
+  const int64_t xs = X - p.v_sink0;
+  const int64_t ns = xs < 0 ? 0 : (xs < p.v_nsink ? xs : int64_t(p.v_nsink));
   const int64_t top = X < p.v_F ? X : p.v_F;
   const int64_t nr = top > p.v_base ? top - p.v_base : 0;
   return int32_t((ns + nr) * p.vT);
@@ -166,6 +167,7 @@ int launch_attention(const AttnArgs& a, void* stream, char* err) {
   p.v_nsink = a.vis.n_sink;
   p.v_base = a.vis.base;
   p.v_F = a.vis.F;
+  p.v_sink0 = a.vis.sink0;
   p.scale = a.scale;
   const dim3 grid(p.n_qblk * a.H);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -80,8 +80,9 @@ struct ScatterP {
   uint8_t* dst[2];
   uint8_t* dst_scales[2];
   int32_t H, D, T, es;       // es: element size in bytes
-  int32_t n_lead, lead_slot0, S, W, slots;
+  int32_t n_lead, lead_slot0, ring_base, W, slots;
   int64_t first_ring;
+  int32_t spill_lo, spill_hi, spill_slot0;
 };
 
 // i / d for 0 <= i < 2^24 and 0 < d < 2^16, via a float reciprocal and one correction step
@@ -97,7 +98,13 @@ __device__ __forceinline__ int32_t fdiv(int32_t i, int32_t d, float inv) {
 __device__ __forceinline__ int32_t slot_of_rank(const ScatterP& p, int32_t r) {
   if (r < p.n_lead) return p.lead_slot0 + r;
   const int32_t k = p.ring0 + (r - p.n_lead);
-  return p.S + (k - p.W * fdiv(k, p.W, p.inv_w));
+  return p.ring_base + (k - p.W * fdiv(k, p.W, p.inv_w));
+}
+
+// Slot that receives the old contents of rank r's destination before it is overwritten
+// (a sink frame leaving the window), or -1.
+__device__ __forceinline__ int32_t spill_slot(const ScatterP& p, int32_t r) {
+  return (r >= p.spill_lo && r < p.spill_hi) ? p.spill_slot0 + (r - p.spill_lo) : -1;
 }
 
 // dense: one workgroup per (token row, K|V), 16-byte units; the row's slot is computed once
@@ -107,15 +114,23 @@ __global__ __launch_bounds__(256) void scatter_dense_kernel(ScatterP p, int32_t 
   const int which = blockIdx.y;
   const int32_t r = tr / p.T, t = tr - r * p.T;
   const int32_t slot = slot_of_rank(p, r);
+  const int32_t spill = spill_slot(p, r);
   const int32_t row_bytes = p.D * p.es;
   const int32_t uph = row_bytes >> 4;
   const uint8_t* src = p.src[which] + int64_t(tr) * units * 16;
   const int64_t head_plane = int64_t(p.slots) * p.T * row_bytes;
   const int64_t dst_row = (int64_t(slot) * p.T + t) * row_bytes;
+  const int64_t spill_row = (int64_t(spill) * p.T + t) * row_bytes;
   for (int32_t u = threadIdx.x; u < units; u += blockDim.x) {
     const int32_t h = u >> uph_log2, cc = u & (uph - 1);
     const uint4 x = *reinterpret_cast<const uint4*>(src + int64_t(u) * 16);
-    *reinterpret_cast<uint4*>(p.dst[which] + h * head_plane + dst_row + cc * 16) = x;
+    uint8_t* dp = p.dst[which] + h * head_plane + dst_row + cc * 16;
+    if (spill >= 0) {
+      // the same thread reads the old 16 bytes, moves them, then overwrites them
+      const uint4 old = *reinterpret_cast<const uint4*>(dp);
+      *reinterpret_cast<uint4*>(p.dst[which] + h * head_plane + spill_row + cc * 16) = old;
+    }
+    *reinterpret_cast<uint4*>(dp) = x;
   }
 }
 
@@ -140,9 +155,21 @@ __global__ __launch_bounds__(256) void scatter_fp4_kernel(ScatterP p, int32_t n_
     quant64(p.src[which] + (int64_t(tr) * units + g) * 128, pk0, pk1, sc);
     const int64_t row = h * head_rows + int64_t(slot_of_rank(p, r)) * p.T + t;
     uint8_t* dp = p.dst[which] + row * (p.D / 2) + cc * 32;
+    uint32_t* sp = reinterpret_cast<uint32_t*>(p.dst_scales[which] + row * (p.D / 16) + cc * 4);
+    const int32_t spill = spill_slot(p, r);
+    if (spill >= 0) {
+      // move the evicted sink frame's codes and scales (bytes, no re-quantisation)
+      const int64_t srow = h * head_rows + int64_t(spill) * p.T + t;
+      const uint4 o0 = reinterpret_cast<const uint4*>(dp)[0], o1 = reinterpret_cast<const uint4*>(dp)[1];
+      const uint32_t os = *sp;
+      uint8_t* sdp = p.dst[which] + srow * (p.D / 2) + cc * 32;
+      reinterpret_cast<uint4*>(sdp)[0] = o0;
+      reinterpret_cast<uint4*>(sdp)[1] = o1;
+      *reinterpret_cast<uint32_t*>(p.dst_scales[which] + srow * (p.D / 16) + cc * 4) = os;
+    }
     reinterpret_cast<uint4*>(dp)[0] = pk0;
     reinterpret_cast<uint4*>(dp)[1] = pk1;
-    *reinterpret_cast<uint32_t*>(p.dst_scales[which] + row * (p.D / 16) + cc * 4) = sc;
+    *sp = sc;
   }
 }
 
@@ -241,11 +268,14 @@ int launch_scatter(const ScatterArgs& a, void* stream, char* err) {
   p.es = a.dtype == 1 ? 2 : 4;
   p.n_lead = a.n_lead;
   p.lead_slot0 = a.lead_slot0;
-  p.S = a.S;
+  p.ring_base = a.ring_base;
   p.W = a.W;
   p.slots = a.slots;
   p.first_ring = a.first_ring;
   p.ring0 = int32_t(a.first_ring % a.W);
+  p.spill_lo = a.spill_lo;
+  p.spill_hi = a.spill_hi;
+  p.spill_slot0 = a.spill_slot0;
   p.inv_w = 1.0f / float(a.W);
   const int32_t n_rows = a.n_frames * a.T;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -35,7 +35,7 @@ int launch_attention(const AttnArgs& a, void*, char* err) {
   if (maybe_fail(err)) return 1;
   Record r{0, {a.dtype, a.H, a.D, a.nq, a.seg[0].n, a.seg[0].fp4, a.seg[0].head_stride,
                a.seg[0].row_stride, a.seg[1].n, a.seg[1].head_stride, a.seg[1].row_stride,
-               a.vis.mode, a.vis.n_sink, a.vis.base, a.vis.F, a.vis.C,
+               a.vis.mode, a.vis.n_sink, a.vis.base, a.vis.F, a.vis.sink0,
                a.ws != nullptr, a.ws_blocks, a.ws_slots, a.n_cu,
                a.qx != nullptr, a.ox != nullptr, a.x.n, a.x.row_stride}};
   g_log.push_back(r);
@@ -44,8 +44,8 @@ int launch_attention(const AttnArgs& a, void*, char* err) {
 
 int launch_scatter(const ScatterArgs& a, void*, char* err) {
   if (maybe_fail(err)) return 1;
-  Record r{1, {a.dtype, a.fp4, a.H, a.D, a.T, a.n_frames, a.n_lead, a.lead_slot0, a.S, a.W,
-               a.first_ring, a.slots, 0, 0, 0, 0}};
+  Record r{1, {a.dtype, a.fp4, a.H, a.D, a.T, a.n_frames, a.n_lead, a.lead_slot0, a.ring_base, a.W,
+               a.first_ring, a.slots, a.spill_lo, a.spill_hi, a.spill_slot0, 0}};
   g_log.push_back(r);
   return 0;
 }

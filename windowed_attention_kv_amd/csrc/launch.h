@@ -25,12 +25,14 @@ struct KeySeg {
 // Visibility of keys to query row i (keys are indexed across seg[0] then seg[1]):
 //   mode 0: every key is visible;
 //   mode 1 (block-causal over held frames): row i is in the held frame of rank r = i / T,
-//     frame fr(r) = r < n_sink ? r : base + (r - n_sink); with X = (fr / C + 1) * C the key
-//     limit is T * (min(n_sink, X) + max(0, min(F, X) - base)); keys j < limit are visible.
+//     frame fr(r) = r < n_sink ? sink0 + r : base + (r - n_sink) (the held sink frames
+//     sink0.. come first, then the window frames base..F-1, all ascending); with
+//     X = (fr / C + 1) * C the key limit is
+//     T * (clamp(X - sink0, 0, n_sink) + max(0, min(F, X) - base)); keys j < limit are visible.
 struct Visibility {
   int32_t mode = 0;
   int32_t T = 0, C = 0, n_sink = 0;
-  int64_t base = 0, F = 0;
+  int64_t base = 0, F = 0, sink0 = 0;
 };
 
 struct AttnArgs {
@@ -65,16 +67,19 @@ inline int64_t split_slots_offset(int64_t ws_blocks) { return (ws_blocks * 4 + 2
 
 // Copy (or FP4-quantise) frames of a [n_frames*T, H, D] token-major K/V pair into cache
 // slots. Source frame r goes to slot slot_of_rank(r):
-//   r < n_lead ? lead_slot0 + r : S + (first_ring + r - n_lead) mod W
-// (the lead frames are sink frames, the rest rotate through the window ring).
+//   r < n_lead ? lead_slot0 + r : ring_base + (first_ring + r - n_lead) mod W
+// (the lead frames are sink frames in sink slots, the rest go to the window slots). For
+// r in [spill_lo, spill_hi) the destination slot's old contents are first moved to slot
+// spill_slot0 + (r - spill_lo) (a sink frame leaving the window).
 struct ScatterArgs {
   int32_t dtype = 0;
   int32_t fp4 = 0;
   int32_t H = 0, D = 0, T = 0;
   int32_t n_frames = 0;
   int32_t n_lead = 0, lead_slot0 = 0;
-  int32_t S = 0, W = 0;
-  int64_t first_ring = 0;   // (frame - S) of the first non-lead frame
+  int32_t ring_base = 0, W = 0;
+  int64_t first_ring = 0;   // frame id of the first non-lead frame (window slot = id mod W)
+  int32_t spill_lo = 0, spill_hi = 0, spill_slot0 = 0;
   const void* k_src = nullptr;
   const void* v_src = nullptr;
   // destination: head-major planes [H][slots*T][D] (dense) or packed/scales (fp4)

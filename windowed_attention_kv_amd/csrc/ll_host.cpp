@@ -70,6 +70,9 @@ ll_status check_desc(const ll_cache_desc* d) {
   if (d->chunk_frames < 1) return fail(LL_EINVAL, "chunk_frames %d", d->chunk_frames);
   if (d->sink_frames < 0) return fail(LL_EINVAL, "sink_frames %d", d->sink_frames);
   if (d->window_frames < 1) return fail(LL_EINVAL, "window_frames %d", d->window_frames);
+  if (d->window_frames < d->chunk_frames)
+    return fail(LL_EUNSUPPORTED, "window_frames %d < chunk_frames %d", d->window_frames,
+                d->chunk_frames);
   if (d->dtype != LL_F32 && d->dtype != LL_BF16) return fail(LL_EINVAL, "dtype %d", d->dtype);
   if (d->kv_format != LL_KV_DENSE && d->kv_format != LL_KV_FP4)
     return fail(LL_EINVAL, "kv_format %d", d->kv_format);
@@ -143,17 +146,23 @@ struct ll_cache {
   int n_cu;
   bool ws_ready;                // split-schedule counters zeroed (on the calls' stream)
   std::vector<int64_t> frames;  // frames committed per layer
+  std::vector<int64_t> shot;    // first frame of the current shot per layer
 };
 
 namespace {
 
 int32_t slots_of(const ll_cache* c) { return c->d.sink_frames + c->d.window_frames; }
 
-int64_t n_sink_held(int64_t F, int64_t S) { return F < S ? F : S; }
-int64_t ring_base(int64_t F, int64_t S, int64_t W) { return F - W > S ? F - W : S; }
-int64_t held_count(int64_t F, int64_t S, int64_t W) {
-  const int64_t w = F - ring_base(F, S, W);
-  return n_sink_held(F, S) + (w > 0 ? w : 0);
+// Slot layout: W window slots, then S sink slots. Frame f enters window slot f mod W; a sink
+// frame of the current shot (first frame B) moves to sink slot W + (f - B) when the window
+// evicts it. Held frames: the spilled sink frames B..B+k-1, then the window frames
+// max(0, F-W)..F-1; their slots are the prefix [0, min(F, W) + k).
+int64_t n_spilled(int64_t F, int64_t S, int64_t W, int64_t B) {
+  return std::min<int64_t>(std::max<int64_t>(F - W - B, 0), S);
+}
+int64_t window_base(int64_t F, int64_t W) { return F > W ? F - W : 0; }
+int64_t held_count(int64_t F, int64_t S, int64_t W, int64_t B) {
+  return std::min<int64_t>(F, W) + n_spilled(F, S, W, B);
 }
 
 uint8_t* plane(const ll_cache* c, int layer, size_t off) {
@@ -181,9 +190,7 @@ ll_status device_status(int rc, const char* what, const char* msg) {
 // Key segment over the cache's filled slot prefix of one layer.
 ll::KeySeg cache_segment(const ll_cache* c, int32_t layer) {
   const ll_cache_desc& d = c->d;
-  const int64_t F = c->frames[layer];
-  const int64_t nvalid = n_sink_held(F, d.sink_frames) +
-                         std::min<int64_t>(std::max<int64_t>(F - d.sink_frames, 0), d.window_frames);
+  const int64_t nvalid = held_count(c->frames[layer], d.sink_frames, d.window_frames, c->shot[layer]);
   ll::KeySeg s;
   s.k = plane(c, layer, c->L.k_off);
   s.v = plane(c, layer, c->L.v_off);
@@ -216,7 +223,7 @@ ll::ScatterArgs scatter_base(const ll_cache* c, int32_t layer) {
   a.H = d.num_heads;
   a.D = d.head_dim;
   a.T = d.tokens_per_frame;
-  a.S = d.sink_frames;
+  a.ring_base = 0;
   a.W = d.window_frames;
   a.slots = slots_of(c);
   a.k_dst = plane(c, layer, c->L.k_off);
@@ -261,6 +268,7 @@ ll_status ll_cache_create(const ll_cache_desc* desc, void* device_mem, size_t de
   c->n_cu = n_cu;
   c->ws_ready = false;
   c->frames.assign(size_t(desc->num_layers), 0);
+  c->shot.assign(size_t(desc->num_layers), 0);
   *out = c;
   return ok();
 }
@@ -273,6 +281,13 @@ ll_status ll_cache_destroy(ll_cache* cache) {
 ll_status ll_cache_reset(ll_cache* cache) {
   if (!cache) return fail(LL_EINVAL, "cache handle is NULL");
   std::fill(cache->frames.begin(), cache->frames.end(), 0);
+  std::fill(cache->shot.begin(), cache->shot.end(), 0);
+  return ok();
+}
+
+ll_status ll_cache_new_shot(ll_cache* cache, int32_t layer) {
+  if (ll_status s = check_layer(cache, layer)) return s;
+  cache->shot[layer] = cache->frames[layer];
   return ok();
 }
 
@@ -360,11 +375,20 @@ ll_status ll_cache_commit(ll_cache* cache, int32_t layer, const void* k, const v
   if (F + C >= (int64_t(1) << 31) - 1)
     return fail(LL_ESTATE, "layer %d has committed %lld frames: frame ids must fit 31 bits", layer,
                 (long long)F);
+  const int64_t W = d.window_frames, B = cache->shot[layer];
   ll::ScatterArgs a = scatter_base(cache, layer);
   a.n_frames = d.chunk_frames;
-  a.n_lead = int32_t(std::min<int64_t>(std::max<int64_t>(S - F, 0), C));
-  a.lead_slot0 = int32_t(F < S ? F : 0);
-  a.first_ring = std::max<int64_t>(F, S) - S;
+  a.n_lead = 0;
+  a.first_ring = F;
+  // frame F+r evicts frame e = F+r-W from its window slot (C <= W, so e < F); a sink frame
+  // of the current shot (B <= e < B+S) moves to sink slot W + (e - B)
+  const int64_t lo = std::max<int64_t>(0, B + W - F);
+  const int64_t hi = std::min<int64_t>(C, B + S + W - F);
+  if (lo < hi) {
+    a.spill_lo = int32_t(lo);
+    a.spill_hi = int32_t(hi);
+    a.spill_slot0 = int32_t(W + (F + lo - W - B));
+  }
   a.k_src = k;
   a.v_src = v;
   char msg[256] = "";
@@ -388,9 +412,10 @@ ll_status ll_recache(ll_cache* cache, int32_t layer, const void* q, const void* 
   const ll_cache_desc& d = cache->d;
   const int64_t F = cache->frames[layer];
   const int64_t S = d.sink_frames, W = d.window_frames;
-  const int64_t held = held_count(F, S, W);
+  const int64_t B = cache->shot[layer];
+  const int64_t held = held_count(F, S, W, B);
   if (held == 0) return fail(LL_ESTATE, "recache of layer %d, which holds no frame", layer);
-  const int64_t nsink = n_sink_held(F, S), base = ring_base(F, S, W);
+  const int64_t nsink = n_spilled(F, S, W, B), base = window_base(F, W);
   const int32_t n = int32_t(held * d.tokens_per_frame);
   char msg[256] = "";
 
@@ -410,6 +435,7 @@ ll_status ll_recache(ll_cache* cache, int32_t layer, const void* q, const void* 
   a.vis.n_sink = int32_t(nsink);
   a.vis.base = base;
   a.vis.F = F;
+  a.vis.sink0 = B;
   a.scale = cache->scale;
   if (ll_status s = device_status(ll::launch_attention(a, stream, msg), "recache attention", msg))
     return s;
@@ -425,8 +451,8 @@ ll_status ll_recache(ll_cache* cache, int32_t layer, const void* q, const void* 
   ll::ScatterArgs w = scatter_base(cache, layer);
   w.n_frames = int32_t(held);
   w.n_lead = int32_t(nsink);
-  w.lead_slot0 = 0;
-  w.first_ring = base - S;
+  w.lead_slot0 = int32_t(W);
+  w.first_ring = base;
   w.k_src = k;
   w.v_src = v;
   if (ll_status s = device_status(ll::launch_scatter(w, stream, msg), "recache rewrite", msg))
@@ -459,9 +485,10 @@ ll_status ll_cache_state(const ll_cache* cache, int32_t layer, int64_t* frames_c
   const int64_t S = cache->d.sink_frames, W = cache->d.window_frames;
   if (frames_committed) *frames_committed = F;
   if (slot_frame) {
+    const int64_t B = cache->shot[layer];
     for (int32_t i = 0; i < slots_of(cache); ++i) slot_frame[i] = -1;
-    for (int64_t f = 0; f < n_sink_held(F, S); ++f) slot_frame[f] = int32_t(f);
-    for (int64_t f = ring_base(F, S, W); f < F; ++f) slot_frame[S + (f - S) % W] = int32_t(f);
+    for (int64_t j = 0; j < n_spilled(F, S, W, B); ++j) slot_frame[W + j] = int32_t(B + j);
+    for (int64_t f = window_base(F, W); f < F; ++f) slot_frame[f % W] = int32_t(f);
   }
   return ok();
 }
