@@ -584,7 +584,7 @@ void attn_bf16_direct_kernel(Params p) {
   const int64_t UT = int64_t(nblk) * tail;
   const int GSELF = p.n_self_wg;
   const int GS = GSELF - nblk;
-  const bool xwg = g >= GSELF;                 // a fused cross-attention workgroup
+  const bool xwg = !FP4 && g >= GSELF;         // a fused cross-attention workgroup
   const bool spare = !xwg && p.split && g >= nblk;
   const int64_t u0 = spare ? range_start(g - nblk, UT, GS) : 0;
   const int64_t u1 = spare ? range_start(g - nblk + 1, UT, GS) : 0;
@@ -643,8 +643,13 @@ void attn_bf16_direct_kernel(Params p) {
     }
 
     // the piece's key segments: self = (cache, own chunk), cross = (x, none)
-    const DevSeg& SA = xjob ? p.x : p.a;
-    const int na = SA.n;
+    // (selected field by field: a runtime-selected reference to a kernel-argument struct
+    // would make the compiler copy the arguments to scratch memory)
+    const uint8_t* const sa_k = xjob ? p.x.k : p.a.k;
+    const uint8_t* const sa_v = xjob ? p.x.v : p.a.v;
+    const int64_t sa_hs = xjob ? p.x.head_stride : p.a.head_stride;
+    const int64_t sa_rs = xjob ? p.x.row_stride : p.a.row_stride;
+    const int na = xjob ? p.x.n : p.a.n;
     const int nb = xjob ? 0 : p.b.n;
     const int row0 = qblk * (NW * 32);
     const int row = row0 + wave * 32 + l32;
@@ -714,12 +719,12 @@ void attn_bf16_direct_kernel(Params p) {
           return;
         }
       }
-      const DevSeg& sg = inA ? SA : p.b;
       const int r0 = (inA ? t : t - ntA) * TR;                  // first row of the tile in the segment
-      const int64_t rp = sg.row_stride * 2;                      // row pitch in bytes
-      const uint8_t* kb0 = sg.k + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
-      const uint8_t* vb0 = sg.v + (h * sg.head_stride) * 2 + int64_t(r0) * rp;
-      const int left = sg.n - r0;                                // rows of this segment from r0 on
+      const int64_t rp = (inA ? sa_rs : p.b.row_stride) * 2;     // row pitch in bytes
+      const int64_t hs = inA ? sa_hs : p.b.head_stride;
+      const uint8_t* kb0 = (inA ? sa_k : p.b.k) + (h * hs) * 2 + int64_t(r0) * rp;
+      const uint8_t* vb0 = (inA ? sa_v : p.b.v) + (h * hs) * 2 + int64_t(r0) * rp;
+      const int left = (inA ? na : nb) - r0;                     // rows of this segment from r0 on
       const uint32_t bytes = left > 0 ? uint32_t(left - 1) * uint32_t(rp) + DT_ROW : 0u;
       const __amdgpu_buffer_rsrc_t rk = rsrc(kb0, bytes), rv = rsrc(vb0, bytes);
 #pragma unroll
@@ -992,6 +997,23 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
     if (cross && (a.vis.mode != 0 || a.x.fp4)) {
       snprintf(err, 256, "fused cross-attention needs an unmasked call and bf16 text keys");
       return 1;
+    }
+    if (cross && fp4) {
+      // the FP4 kernel is built without cross blocks (fewer live scalar registers): the self
+      // part, then the cross part as a dense launch
+      AttnArgs self = a;
+      self.qx = nullptr;
+      self.ox = nullptr;
+      self.x = KeySeg{};
+      if (int r = launch_attention_bf16(self, stream, err)) return r;
+      AttnArgs cx = self;
+      cx.q = a.qx;
+      cx.o = a.ox;
+      cx.seg[0] = a.x;
+      cx.seg[1] = a.x;
+      cx.seg[1].n = 0;
+      cx.ws = nullptr;
+      return launch_attention_bf16(cx, stream, err);
     }
     if (a.vis.mode == 0 && a.ws && a.n_cu > blocks && blocks <= a.ws_blocks) {
       // Split when the best main/tail cut is clearly shorter than one whole block. Cost in

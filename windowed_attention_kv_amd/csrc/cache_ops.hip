@@ -121,16 +121,23 @@ __global__ __launch_bounds__(256) void scatter_dense_kernel(ScatterP p, int32_t 
   const int64_t head_plane = int64_t(p.slots) * p.T * row_bytes;
   const int64_t dst_row = (int64_t(slot) * p.T + t) * row_bytes;
   const int64_t spill_row = (int64_t(spill) * p.T + t) * row_bytes;
+  if (spill >= 0) {
+    // a sink frame leaves the window: the same thread reads the old 16 bytes, moves them to
+    // the sink slot, then overwrites them (rare rows; the common loop below stays plain)
+    for (int32_t u = threadIdx.x; u < units; u += blockDim.x) {
+      const int32_t h = u >> uph_log2, cc = u & (uph - 1);
+      const uint4 x = *reinterpret_cast<const uint4*>(src + int64_t(u) * 16);
+      uint8_t* dp = p.dst[which] + h * head_plane + dst_row + cc * 16;
+      const uint4 old = *reinterpret_cast<const uint4*>(dp);
+      *reinterpret_cast<uint4*>(p.dst[which] + h * head_plane + spill_row + cc * 16) = old;
+      *reinterpret_cast<uint4*>(dp) = x;
+    }
+    return;
+  }
   for (int32_t u = threadIdx.x; u < units; u += blockDim.x) {
     const int32_t h = u >> uph_log2, cc = u & (uph - 1);
     const uint4 x = *reinterpret_cast<const uint4*>(src + int64_t(u) * 16);
-    uint8_t* dp = p.dst[which] + h * head_plane + dst_row + cc * 16;
-    if (spill >= 0) {
-      // the same thread reads the old 16 bytes, moves them, then overwrites them
-      const uint4 old = *reinterpret_cast<const uint4*>(dp);
-      *reinterpret_cast<uint4*>(p.dst[which] + h * head_plane + spill_row + cc * 16) = old;
-    }
-    *reinterpret_cast<uint4*>(dp) = x;
+    *reinterpret_cast<uint4*>(p.dst[which] + h * head_plane + dst_row + cc * 16) = x;
   }
 }
 
@@ -145,6 +152,30 @@ __global__ __launch_bounds__(256) void scatter_fp4_kernel(ScatterP p, int32_t n_
   const int32_t tr0 = p.row0 + blockIdx.x * kFp4Rows;
   const int32_t nrows = n_units / units;
   const int32_t nr = min(kFp4Rows, p.row0 + nrows - tr0);
+  // frame ranks of this workgroup's rows; when one of them moves a sink frame out of the
+  // window, a first pass moves the old codes and scales (bytes, no re-quantisation) to the
+  // sink slot before any of them is overwritten (rare; the common pass stays plain)
+  const int32_t r_first = tr0 / p.T, r_last = (tr0 + nr - 1) / p.T;
+  if (r_last >= p.spill_lo && r_first < p.spill_hi) {
+    for (int32_t i = threadIdx.x; i < nr * units; i += blockDim.x) {
+      const int32_t rl = i / units, g = i - rl * units;
+      const int32_t tr = tr0 + rl;
+      const int32_t r = tr / p.T, t = tr - r * p.T;
+      const int32_t spill = spill_slot(p, r);
+      if (spill < 0) continue;
+      const int32_t h = g >> gph_log2, cc = g & ((1 << gph_log2) - 1);
+      const int64_t row = h * head_rows + int64_t(slot_of_rank(p, r)) * p.T + t;
+      const int64_t srow = h * head_rows + int64_t(spill) * p.T + t;
+      const uint4* dp = reinterpret_cast<const uint4*>(p.dst[which] + row * (p.D / 2) + cc * 32);
+      uint4* sdp = reinterpret_cast<uint4*>(p.dst[which] + srow * (p.D / 2) + cc * 32);
+      const uint4 o0 = dp[0], o1 = dp[1];
+      const uint32_t os = *reinterpret_cast<const uint32_t*>(p.dst_scales[which] + row * (p.D / 16) + cc * 4);
+      sdp[0] = o0;
+      sdp[1] = o1;
+      *reinterpret_cast<uint32_t*>(p.dst_scales[which] + srow * (p.D / 16) + cc * 4) = os;
+    }
+    __syncthreads();
+  }
   for (int32_t i = threadIdx.x; i < nr * units; i += blockDim.x) {
     const int32_t rl = i / units, g = i - rl * units;
     const int32_t tr = tr0 + rl;
@@ -155,21 +186,9 @@ __global__ __launch_bounds__(256) void scatter_fp4_kernel(ScatterP p, int32_t n_
     quant64(p.src[which] + (int64_t(tr) * units + g) * 128, pk0, pk1, sc);
     const int64_t row = h * head_rows + int64_t(slot_of_rank(p, r)) * p.T + t;
     uint8_t* dp = p.dst[which] + row * (p.D / 2) + cc * 32;
-    uint32_t* sp = reinterpret_cast<uint32_t*>(p.dst_scales[which] + row * (p.D / 16) + cc * 4);
-    const int32_t spill = spill_slot(p, r);
-    if (spill >= 0) {
-      // move the evicted sink frame's codes and scales (bytes, no re-quantisation)
-      const int64_t srow = h * head_rows + int64_t(spill) * p.T + t;
-      const uint4 o0 = reinterpret_cast<const uint4*>(dp)[0], o1 = reinterpret_cast<const uint4*>(dp)[1];
-      const uint32_t os = *sp;
-      uint8_t* sdp = p.dst[which] + srow * (p.D / 2) + cc * 32;
-      reinterpret_cast<uint4*>(sdp)[0] = o0;
-      reinterpret_cast<uint4*>(sdp)[1] = o1;
-      *reinterpret_cast<uint32_t*>(p.dst_scales[which] + srow * (p.D / 16) + cc * 4) = os;
-    }
     reinterpret_cast<uint4*>(dp)[0] = pk0;
     reinterpret_cast<uint4*>(dp)[1] = pk1;
-    *sp = sc;
+    *reinterpret_cast<uint32_t*>(p.dst_scales[which] + row * (p.D / 16) + cc * 4) = sc;
   }
 }
 
