@@ -544,7 +544,7 @@ def main():
                      # Q and O (n x H x D bf16 each) + the visible keys' K and V: per launch the
                      # K/V bytes are 2 * keys * H * D * 2 = flops_per_launch / n
                      "algorithmic_bytes_per_launch": round(2 * n * H * D * 2 + attn_flops_launch / n),
-                     "kernel": "attn_bf16_direct_kernel<8,2,false>",
+                     "kernel": "attn_bf16_direct_kernel<8,2,false,false>",
                      "avg_launch_ms": round(attn_ms, 4),
                      "avg_flops_per_launch": attn_flops_launch},
         "rows": {"commit": {"avg_launch_ms": round(commit_ms, 5), "bytes": commit_bytes,

@@ -518,7 +518,7 @@ struct SplitState {
 __device__ __forceinline__ int64_t range_start(int64_t g, int64_t U, int64_t G) { return g * U / G; }
 __device__ __forceinline__ int64_t range_of(int64_t u, int64_t U, int64_t G) { return ((u + 1) * G - 1) / U; }
 
-template <int NW, int SUB, bool FP4>
+template <int NW, int SUB, bool FP4, bool CROSS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_direct_kernel(Params p) {
   constexpr int D = 128;
@@ -584,7 +584,7 @@ void attn_bf16_direct_kernel(Params p) {
   const int64_t UT = int64_t(nblk) * tail;
   const int GSELF = p.n_self_wg;
   const int GS = GSELF - nblk;
-  const bool xwg = !FP4 && g >= GSELF;         // a fused cross-attention workgroup
+  const bool xwg = CROSS && g >= GSELF;        // a fused cross-attention workgroup
   const bool spare = !xwg && p.split && g >= nblk;
   const int64_t u0 = spare ? range_start(g - nblk, UT, GS) : 0;
   const int64_t u1 = spare ? range_start(g - nblk + 1, UT, GS) : 0;
@@ -845,33 +845,31 @@ void attn_bf16_direct_kernel(Params p) {
       if (!s_last) continue;
       // merge: the main piece, then the tail pieces in range order (the result does not
       // depend on which workgroup merges)
+      // Reads use buffer loads with the agent-scope (sc1) cache policy, the encoding of an
+      // agent-scope atomic load; as plain loads they may be issued back to back. Pass 1
+      // takes the largest running max, pass 2 sums the rescaled pieces.
+      const __amdgpu_buffer_rsrc_t rpart = rsrc(p.part, 0xFFFFFFFFu);
+      auto slot_of_piece = [&](int gs) { return gs < gs_first ? blk : nblk + gs + blk; };
+      auto ld = [&](int sl, int r) {
+        const uint32_t off = uint32_t((int64_t(sl) * SS::SLOT_FLOATS + r * NW * 64 + wave * 64 + lane) * 4);
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, off, 0, 16));
+      };
+      float m_all = -__builtin_inff();
+      for (int gs = gs_first - 1; gs <= gs_last; ++gs) m_all = fmaxf(m_all, ld(slot_of_piece(gs), 64));
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16_t{};
+      l_run = 0.f;
       for (int gs = gs_first - 1; gs <= gs_last; ++gs) {
-        const int sl = gs < gs_first ? blk : nblk + gs + blk;
-        const float* rp = p.part + int64_t(sl) * SS::SLOT_FLOATS + wave * 64 + lane;
-        auto ld = [&](int r) {
-          return __hip_atomic_load(rp + r * NW * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        };
-        const float m_p = ld(64);
-        const float l_p = ld(65);
-        if (gs < gs_first) {
+        const int sl = slot_of_piece(gs);
+        const float m_p = ld(sl, 64);
+        const float f = m_p == m_all ? 1.0f : __builtin_amdgcn_exp2f(m_p - m_all);
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[db][i] = ld(db * 16 + i);
-          m_run = m_p;
-          l_run = l_p;
-        } else {
-          const float mn = fmaxf(m_run, m_p);
-          const float fa = m_run == mn ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
-          const float fb = m_p == mn ? 1.0f : __builtin_amdgcn_exp2f(m_p - mn);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[db][i] = oacc[db][i] * fa + ld(db * 16 + i) * fb;
-          l_run = l_run * fa + l_p * fb;
-          m_run = mn;
-        }
+          for (int i = 0; i < 16; ++i) oacc[db][i] += ld(sl, db * 16 + i) * f;
+        l_run += ld(sl, 65) * f;
       }
+      m_run = m_all;
     }
 
     {
@@ -895,9 +893,9 @@ void attn_bf16_direct_kernel(Params p) {
   }
 }
 
-template <int NW, int SUB, bool FP4>
+template <int NW, int SUB, bool FP4, bool CROSS>
 int launch_direct(const Params& p, int grid, hipStream_t stream, char* err) {
-  auto kern = attn_bf16_direct_kernel<NW, SUB, FP4>;
+  auto kern = attn_bf16_direct_kernel<NW, SUB, FP4, CROSS>;
   constexpr int DT_LDS = DtCfg<SUB>::LDS + (FP4 ? BN * DT_ROW : 0);
   static bool attr_set = false;
   if (!attr_set) {
@@ -1018,10 +1016,10 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
     if (a.vis.mode == 0 && a.ws && a.n_cu > blocks && blocks <= a.ws_blocks) {
       // Split when the best main/tail cut is clearly shorter than one whole block. Cost in
       // key tiles, with kPieceCost tiles per piece for its prologue (Q load, first tile not
-      // overlapped) and its publish; a spare workgroup runs at most ceil(span/tail) + 1
-      // pieces. Measured on MI355X: 12 heads x 4680 rows (228 blocks) is faster whole, 3
-      // heads (57 blocks) about 4x faster split.
-      constexpr int64_t kPieceCost = 5;
+      // overlapped) and its publish (a spare workgroup runs at most ceil(span/tail) + 1
+      // pieces), and kMergeCost per piece the merging workgroup reads. Measured on MI355X:
+      // 12 heads x 4680 rows (228 blocks) is faster whole, 1-6 heads are faster split.
+      constexpr int64_t kPieceCost = 5, kMergeCost = 1;
       const int nt = (p.a.n + TR - 1) / TR + (p.b.n + TR - 1) / TR;
       const int64_t spare = a.n_cu - blocks;
       int best_main = nt;
@@ -1033,7 +1031,9 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
         const int64_t span = (ut + gs - 1) / gs;
         const int64_t c_main = m + kPieceCost;
         const int64_t c_spare = span + kPieceCost * ((span + tail - 1) / tail + 1);
-        const int64_t mk = c_main > c_spare ? c_main : c_spare;
+        // the last workgroup of a block then reads every piece of it (main + tails)
+        const int64_t merge = kMergeCost * ((tail + span - 1) / span + 2);
+        const int64_t mk = (c_main > c_spare ? c_main : c_spare) + merge;
         if (mk < best) {
           best = mk;
           best_main = m;
@@ -1061,8 +1061,11 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
       p.ox = static_cast<uint16_t*>(a.ox);
       p.x = seg(a.x);
     }
-    return fp4 ? launch_direct<DNW, DSUB, true>(p, p.n_wg, s, err)
-               : launch_direct<DNW, DSUB, false>(p, p.n_wg, s, err);
+    // cross blocks only exist in their own instantiation, so the common kernels carry no
+    // cross fields or per-piece segment selection
+    if (cross) return launch_direct<DNW, DSUB, false, true>(p, p.n_wg, s, err);
+    return fp4 ? launch_direct<DNW, DSUB, true, false>(p, p.n_wg, s, err)
+               : launch_direct<DNW, DSUB, false, false>(p, p.n_wg, s, err);
   }
   if (a.D == 64) {
     return fp4 ? launch_t<64, NW, true>(p, p.n_wg, s, err) : launch_t<64, NW, false>(p, p.n_wg, s, err);
