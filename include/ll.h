@@ -78,7 +78,7 @@ typedef struct {
 typedef struct ll_cache ll_cache; /* opaque host handle */
 
 /* Bytes of device memory a cache with this descriptor needs: S+W frame slots per layer for K
- * and V (dense or FP4 planes), and, for a dense bf16 head_dim-128 cache, a workspace after
+ * and V (dense or FP4 planes), and, for a bf16 head_dim-128 cache, a workspace after
  * the last layer for the split schedule of ll_attn_chunk (used when a call has fewer
  * (head, 256-row query block) pairs than the device has compute units, e.g. a few heads per
  * GPU): one 32-bit counter per (head, query block), padded to 256 bytes, then

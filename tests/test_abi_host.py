@@ -273,8 +273,8 @@ def _split_workspace(H, n, cache_keys, n_cu):
 
 def test_cache_bytes():
     """Cache size depends only on S+W (and the shape), per layer: 12 frames of 1560 tokens x
-    12 heads x 128 in bf16, K and V = 115.0 MB, plus the split-schedule workspace (the
-    recording backend reports 256 CUs); FP4: 4.5 bits per element, no workspace."""
+    12 heads x 128 in bf16, K and V = 115.0 MB, plus one split-schedule workspace per cache
+    (the recording backend reports 256 CUs); FP4: 4.5 bits per element."""
     if not os.path.exists(_lib.FAKE_PATH):
         pytest.skip("libll_fake.so not built")
     f = _lib.load_fake()
@@ -285,7 +285,7 @@ def test_cache_bytes():
     d = make_desc(30, 12, 128, 1560, 3, 3, 9, kv_format="fp4")
     assert f.ll_cache_size(ctypes.byref(d), ctypes.byref(size)) == 0
     elems = 12 * 1560 * 12 * 128
-    assert size.value == 30 * 2 * (elems // 2 + elems // 16)
+    assert size.value == 30 * 2 * (elems // 2 + elems // 16) + _split_workspace(12, 4680, 12 * 1560, 256)
 
 
 def test_split_workspace_is_cleared_once_and_passed_to_chunk_attention(fake):
@@ -318,8 +318,8 @@ def test_split_workspace_is_cleared_once_and_passed_to_chunk_attention(fake):
     assert fake.ll_attn_chunk(h2, 0, P, P, P, P, None) == _lib.LL_EDEVICE
     assert fake.ll_attn_chunk(h2, 0, P, P, P, P, None) == 0
     assert [k for k, _ in _records(fake)] == [4, 0]
-    # fp32, head_dim 64 and FP4 caches have no workspace
-    for other in (dict(dtype="f32"), dict(head_dim=64), dict(kv_format="fp4")):
+    # fp32 and head_dim 64 caches have no workspace (an FP4 store has the same one)
+    for other in (dict(dtype="f32"), dict(head_dim=64)):
         h3, size3 = _create(fake, **{**kw, **other})
         fake.llfake_reset()
         assert fake.ll_attn_chunk(h3, 0, P, P, P, P, None) == 0

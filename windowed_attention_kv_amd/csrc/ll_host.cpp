@@ -49,8 +49,8 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t k_off, v_off, ks_off, vs_off;  // byte offsets inside one layer
   size_t layer_bytes;
-  // workspace of the split attention schedule, after the last layer (dense bf16 head_dim
-  // 128 only): arrival counters for every (head, query block) of a chunk call, then two
+  // workspace of the split attention schedule, after the last layer (bf16 head_dim 128,
+  // dense or FP4 store): arrival counters for every (head, query block) of a chunk call, then two
   // piece-state slots per workgroup of the largest split launch
   size_t ws_bytes;
   int32_t ws_blocks, ws_slots;
@@ -118,7 +118,7 @@ Layout layout_of(const ll_cache_desc* d, int n_cu) {
   }
   L.ws_bytes = 0;
   L.ws_blocks = L.ws_slots = 0;
-  if (d->kv_format == LL_KV_DENSE && d->dtype == LL_BF16 && d->head_dim == 128 && n_cu > 0) {
+  if (d->dtype == LL_BF16 && d->head_dim == 128 && n_cu > 0) {
     const int64_t n = int64_t(d->chunk_frames) * d->tokens_per_frame;
     const int64_t blocks = int64_t(d->num_heads) * ((n + ll::kSplitRows - 1) / ll::kSplitRows);
     const int64_t nt = (int64_t(slots) * d->tokens_per_frame + ll::kSplitKeys - 1) / ll::kSplitKeys +
