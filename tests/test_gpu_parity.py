@@ -416,3 +416,58 @@ def test_recache_after_a_new_shot():
         model.commit(kk.values, vv.values, kk.bits, vv.bits)
         _check_export(cache, model, shape)
 
+
+def test_stack_config_sampled():
+    """The stack workload as the bench runs it (one 30-layer cache; per chunk 4 denoise steps
+    over all layers, the last step commits), for 16 chunks (fill-up, the window's wrap and
+    the sink retiring into its slots). Layers 0, 15 and 29 take seeded inputs and are checked
+    against per-layer oracles on sampled rows of chunks 0, 1, 4, 5 and 15 (steps 0 and 3);
+    the other layers take resident random inputs. At the end every layer's exported cache
+    equals, bit for bit, the K/V committed into each slot."""
+    import torch
+    shape = synth.CONFIGS["layer"]
+    L, steps, n_chunks = 30, 4, 16
+    C, S, W, T = shape.chunk_frames, shape.sink_frames, shape.window_frames, shape.tokens_per_frame
+    n, H, D = shape.n_query, shape.heads, shape.head_dim
+    sampled_layers, sampled_chunks, sampled_steps = (0, 15, 29), {0, 1, 4, 5, 15}, {0, 3}
+    rows = sample_rows(n, 16, seed=9)
+    log("case: stack config, 30 layers x 4 steps x 16 chunks, sampled layers/chunks/rows")
+    cache = _cache(shape, layers=L)
+    models = {l: _model(shape) for l in sampled_layers}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    pool = [tuple((torch.randn((n, H, D), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+                  for _ in range(3)) for _ in range(4)]
+    committed = {}          # (layer, chunk) -> (k, v) device tensors committed
+    for c in range(n_chunks):
+        for st in range(steps):
+            for layer in range(L):
+                last = st == steps - 1
+                if layer in models and (last or (c in sampled_chunks and st in sampled_steps)):
+                    q, k, v = synth.chunk_inputs(shape, layer, st, c)
+                    tq, tk, tv = q.torch("cuda"), k.torch("cuda"), v.torch("cuda")
+                    o = cache.attn_chunk(layer, tq, tk, tv)
+                    if c in sampled_chunks and st in sampled_steps:
+                        ref = models[layer].attn_chunk(q.values, k.values, v.values, rows=rows)
+                        assert_close(to_np(o)[rows], ref, "bf16", f"layer {layer} chunk {c} step {st}")
+                    if last:
+                        models[layer].commit(k.values, v.values, k.bits, v.bits)
+                else:
+                    tq, tk, tv = pool[(c * steps * L + st * L + layer) % len(pool)]
+                    cache.attn_chunk(layer, tq, tk, tv)
+                if last:
+                    cache.commit(layer, tk, tv)
+                    committed[(layer, c)] = (tk, tv)
+    torch.cuda.synchronize()
+    F = n_chunks * C
+    slot_frames = ring.slot_map(F, S, W)
+    for layer in range(L):
+        K, V = cache.export(layer)
+        Fs, slots = cache.state(layer)
+        assert Fs == F and slots == slot_frames
+        for slot, f in enumerate(slot_frames):
+            tk, tv = committed[(layer, f // C)]
+            i = f % C
+            assert torch.equal(K[slot * T:(slot + 1) * T], tk[i * T:(i + 1) * T]), (layer, slot, f)
+            assert torch.equal(V[slot * T:(slot + 1) * T], tv[i * T:(i + 1) * T]), (layer, slot, f)
+
