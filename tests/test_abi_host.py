@@ -145,12 +145,13 @@ def test_recache_launches(fake, chunks):
     fake.llfake_reset()
     assert fake.ll_recache(h, 0, P, P, P, P, P, P, 512, P, P, None) == 0
     recs = _records(fake)
-    assert [k for k, _ in recs] == [0, 0, 1]
-    self_att, cross, rewrite = recs[0][1], recs[1][1], recs[2][1]
+    assert [k for k, _ in recs] == [0, 1]
+    self_att, rewrite = recs[0][1], recs[1][1]
     assert self_att[3] == len(held) * T and self_att[4] == len(held) * T and self_att[11] == 1
     assert self_att[12] == ring.n_spilled(F, S, W) and self_att[13] == max(0, F - W)
     assert self_att[14] == F and self_att[15] == 0
-    assert cross[3] == len(held) * T and cross[4] == 512 and cross[11] == 0
+    # the cross-attention to the 512 text keys rides in the same launch
+    assert self_att[20:23] == [1, 1, 512] and self_att[16] == 0
     assert rewrite[5] == len(held)
     assert rewrite[12] == rewrite[13]          # no spill
     for r, f in enumerate(held):
@@ -203,7 +204,7 @@ def test_recache_after_a_new_shot(fake):
     assert held == [12, 13, 14] + list(range(21, 27))
     fake.llfake_reset()
     assert fake.ll_recache(h, 0, P, P, P, P, P, P, 64, P, P, None) == 0
-    self_att, cross, rewrite = (f for _, f in _records(fake))
+    self_att, rewrite = (f for _, f in _records(fake))
     assert self_att[3] == len(held) * T and self_att[12:16] == [3, 21, 27, 12]
     for r, f in enumerate(held):
         assert _kernel_slot(rewrite, r) == ring.slot_of_frame(f, F, S, W, B)
@@ -310,7 +311,7 @@ def test_split_workspace_is_cleared_once_and_passed_to_chunk_attention(fake):
     fake.llfake_reset()
     assert fake.ll_recache(h, 0, P, P, P, P, P, P, 7, P, P, None) == 0
     atts = [f for k, f in _records(fake) if k == 0]
-    assert len(atts) == 2 and all(f[16] == 0 for f in atts)
+    assert len(atts) == 1 and atts[0][16] == 0 and atts[0][22] == 7
     # a failed clear leaves the workspace uncleared: the next call clears it
     h2, _ = _create(fake, **kw)
     fake.llfake_reset()

@@ -992,8 +992,8 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
     const int blocks = p.n_qblk * a.H;
     p.n_wg = blocks;
     const bool cross = a.qx != nullptr && a.x.n > 0;
-    if (cross && (a.vis.mode != 0 || a.x.fp4)) {
-      snprintf(err, 256, "fused cross-attention needs an unmasked call and bf16 text keys");
+    if (cross && a.x.fp4) {
+      snprintf(err, 256, "fused cross-attention needs bf16 text keys");
       return 1;
     }
     if (cross && fp4) {

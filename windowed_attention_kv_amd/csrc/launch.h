@@ -50,9 +50,9 @@ struct AttnArgs {
   void* ws = nullptr;
   int32_t ws_blocks = 0, ws_slots = 0;
   int32_t n_cu = 0;         // compute units of the device
-  // optional cross-attention of the same launch (mode 0 only): ox = softmax(scale qx K_x^T)
-  // V_x over segment x, for the same nq rows and heads; fused into the head_dim-128 bf16
-  // kernel, a second launch otherwise
+  // optional cross-attention of the same launch: ox = softmax(scale qx K_x^T) V_x over all of
+  // segment x (never masked), for the same nq rows and heads; fused into the head_dim-128
+  // bf16 kernel, a second launch otherwise
   const void* qx = nullptr;
   void* ox = nullptr;
   KeySeg x;

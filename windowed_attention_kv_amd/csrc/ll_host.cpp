@@ -437,15 +437,12 @@ ll_status ll_recache(ll_cache* cache, int32_t layer, const void* q, const void* 
   a.vis.F = F;
   a.vis.sink0 = B;
   a.scale = cache->scale;
+  // (ii) cross-attention to the new prompt's text tokens, in the same launch
+  a.qx = qx;
+  a.ox = ox;
+  a.x = input_segment(d, k_text, v_text, n_text);
+  a.n_cu = cache->n_cu;
   if (ll_status s = device_status(ll::launch_attention(a, stream, msg), "recache attention", msg))
-    return s;
-  // (ii) cross-attention to the new prompt's text tokens
-  ll::AttnArgs x = a;
-  x.q = qx;
-  x.o = ox;
-  x.seg[0] = input_segment(d, k_text, v_text, n_text);
-  x.vis = ll::Visibility{};
-  if (ll_status s = device_status(ll::launch_attention(x, stream, msg), "recache cross-attention", msg))
     return s;
   // (iii) rewrite every held frame's slot with the new K/V
   ll::ScatterArgs w = scatter_base(cache, layer);
