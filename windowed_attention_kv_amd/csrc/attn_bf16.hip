@@ -21,7 +21,9 @@
 //    loop is identical for both cache formats ("LongLive 2.0" distributed-inference page,
 //    NVFP4 and KV cache section: fused dequantisation);
 //  * workgroups are mapped so that each XCD (own L2) works on a contiguous range of
-//    (head, query block) tiles: the query blocks of one head share their K/V in one L2.
+//    (head, query block) tiles: the query blocks of one head share their K/V in one L2;
+//    block-causal (recache) launches instead dispatch the heaviest block rank of every head
+//    first, longest job first over the whole grid.
 // Two kernels: attn_bf16_direct_kernel (head_dim 128: 8 waves, 128-key tiles loaded straight
 // into LDS, V read with transposing LDS reads, optional split schedule for calls with fewer
 // query blocks than CUs) and attn_bf16_kernel (head_dim 64: 4 waves, 64-key tiles staged
@@ -348,9 +350,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int xcd = bid & 7, idx = bid >> 3;
   const int qd = G >> 3, rm = G & 7;
   const int tile_id = (xcd < rm ? xcd * (qd + 1) : rm * (qd + 1) + (xcd - rm) * qd) + idx;
-  const int h = tile_id / p.n_qblk;
-  // heavy-first inside a head: later query blocks see more keys under the block-causal mask
-  const int qblk = p.n_qblk - 1 - (tile_id % p.n_qblk);
+  // block-causal: heaviest block rank of every head first, in dispatch (workgroup id) order
+  const int h = p.vis_mode == 1 ? int(blockIdx.x) % p.H : tile_id / p.n_qblk;
+  const int qblk = p.n_qblk - 1 - (p.vis_mode == 1 ? int(blockIdx.x) / p.H : tile_id % p.n_qblk);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -634,9 +636,16 @@ void attn_bf16_direct_kernel(Params p) {
     } else {
       if (single_done) break;
       single_done = true;
-      h = g / p.n_qblk;
-      // heavy-first inside a head: later query blocks see more keys under the block-causal mask
-      qblk = p.n_qblk - 1 - (g % p.n_qblk);
+      if (p.vis_mode == 1) {
+        // block-causal: later query blocks see more keys. Dispatch order is the workgroup id,
+        // so the heaviest block rank of every head goes first (longest job first over the
+        // whole grid), spread round-robin over the XCDs
+        h = bid % p.H;
+        qblk = p.n_qblk - 1 - bid / p.H;
+      } else {
+        h = g / p.n_qblk;
+        qblk = p.n_qblk - 1 - (g % p.n_qblk);
+      }
       t0 = 0;
       t1 = -1;  // all of the block's tiles, set below
       whole = true;
