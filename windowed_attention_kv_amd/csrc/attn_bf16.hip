@@ -484,6 +484,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // as zeros through the buffer resource's range check and masked.
 // ---------------------------------------------------------------------------------------
 constexpr int DT_ROW = 256;                 // bytes per key row (128 bf16)
+// MFMA operand reads in flight ahead of the MFMA that uses them; scheduling-group masks of
+// the AMDGPU backend (MFMA, LDS read)
+constexpr int kPipe = 4;
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 // LDS plan of the direct kernel: SUB 64-key sub-tiles per barrier, K then V, double-buffered
 template <int SUB>
@@ -493,6 +497,15 @@ struct DtCfg {
   static constexpr int BUF = 2 * TILE;
   static constexpr int LDS = 2 * BUF;
 };
+
+// Transposing LDS read (ds_read_b64_tr_b16). Reached through a restrict pointer, the call
+// carries alias-scope metadata like a plain load does; without it the backend makes every
+// such read wait for all direct-to-LDS loads in flight, including the next tile's, which
+// writes the other buffer. The kernel orders its LDS buffers itself (wait + barrier before
+// a loaded tile is read).
+__device__ __forceinline__ v4i16_t lds_read_tr(const uint8_t* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+}
 
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
@@ -764,15 +777,29 @@ void attn_bf16_direct_kernel(Params p) {
       if (!FP4 && seg_left <= 0) continue;
       const int key0 = (inA ? 0 : na) + r0;
 
+      // S^T = K Q^T: 16 MFMAs, each fed by one 16-byte LDS read. The reads run kPipe MFMAs
+      // ahead of their use (pinned by the scheduling groups below), so the LDS latency hides
+      // behind the matrix pipe instead of stalling every MFMA.
       f32x16_t s[2];
+      s[0] = f32x16_t{};
+      s[1] = f32x16_t{};
+      {
+        constexpr int NS = 2 * (D / 16);
+        bf16x8_t ka[NS];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16_t{};
+        for (int i = 0; i < NS; ++i)
+          ka[i] = *reinterpret_cast<const bf16x8_t*>(kt + kbase[i % (D / 16)] + (i / (D / 16)) * 32 * DT_ROW);
 #pragma unroll
-        for (int ss = 0; ss < D / 16; ++ss) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + kbase[ss] + kb * 32 * DT_ROW);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ss], s[kb], 0, 0, 0);
+        for (int i = 0; i < NS; ++i)
+          s[i / (D / 16)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qreg[i % (D / 16)],
+                                                                   s[i / (D / 16)], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPipe, 0);
+#pragma unroll
+        for (int i = 0; i < NS - kPipe; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPipe, 0);
       }
       if constexpr (FP4) {
         // next tile's FP4 data -> bf16 while the QK products run; when the next tile is not
@@ -799,21 +826,30 @@ void attn_bf16_direct_kernel(Params p) {
       bf16x8_t pb[2][2];
       softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
 
+      // O^T += V^T P^T: 16 MFMAs, each fed by two transposing LDS reads, pipelined like S
+      {
+        constexpr int NP = (D / 32) * 4;
+        bf16x8_t va[NP];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+        for (int i = 0; i < NP; ++i) {
+          const int db = i / 4, kb = (i / 2) & 1, j = i & 1;
+          const uint8_t* a0 = vt + vbase[db] + (kb * 32 + 16 * j) * DT_ROW;
+          const v4i16_t lo = lds_read_tr(a0);
+          const v4i16_t hi4 = lds_read_tr(a0 + 8 * DT_ROW);
+          va[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < NP; ++i) {
+          const int db = i / 4, kb = (i / 2) & 1, j = i & 1;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[kb][j], oacc[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPipe, 0);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const uint8_t* a0 = vt + vbase[db] + (kb * 32 + 16 * j) * DT_ROW;
-            const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16_t*)(a0));
-            const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16_t*)(a0 + 8 * DT_ROW));
-            const bf16x8_t a = __builtin_bit_cast(
-                bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][j], oacc[db], 0, 0, 0);
-          }
+        for (int i = 0; i < NP - kPipe; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPipe, 0);
       }
       }
 
