@@ -780,6 +780,11 @@ void attn_bf16_direct_kernel(Params p) {
       // S^T = K Q^T: 16 MFMAs, each fed by one 16-byte LDS read. The reads run kPipe MFMAs
       // ahead of their use (pinned by the scheduling groups below), so the LDS latency hides
       // behind the matrix pipe instead of stalling every MFMA.
+      // Wave priority (dense tiles): raised for the MFMA blocks, lowered for the softmax, so
+      // that of the two waves sharing a SIMD the one with MFMAs to issue wins and the other's
+      // VALU work fills the matrix pipe's shadow; that pulls the pair out of phase. (FP4
+      // tiles, whose dequantisation sits in the QK block, run slower with it.)
+      if constexpr (!FP4) __builtin_amdgcn_s_setprio(1);
       f32x16_t s[2];
       s[0] = f32x16_t{};
       s[1] = f32x16_t{};
@@ -824,7 +829,9 @@ void attn_bf16_direct_kernel(Params p) {
       }
 
       bf16x8_t pb[2][2];
+      if constexpr (!FP4) __builtin_amdgcn_s_setprio(0);
       softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
+      if constexpr (!FP4) __builtin_amdgcn_s_setprio(1);
 
       // O^T += V^T P^T: 16 MFMAs, each fed by two transposing LDS reads, pipelined like S
       {
@@ -851,6 +858,7 @@ void attn_bf16_direct_kernel(Params p) {
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPipe, 0);
       }
+      if constexpr (!FP4) __builtin_amdgcn_s_setprio(0);
       }
 
       __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of tile t+1 have landed
