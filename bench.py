@@ -299,6 +299,29 @@ def commit_batch_row(torch, shape, Cache, kv_format, k, v):
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def copy_ceiling_row(torch, k, v):
+    """Context for the commit rows: a plain device copy (torch's copy kernel) of the same K and V
+    a dense commit moves, 2 x 14.38 MB read and written; per-copy time of 30 back-to-back pairs
+    of copies, events bracketing each batch like commit_batch_row."""
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    for _ in range(3):
+        dk.copy_(k)
+        dv.copy_(v)
+    tm = EventTimer(torch)
+    for rep in range(10):
+        s = tm.start()
+        for _ in range(30):
+            dk.copy_(k)
+            dv.copy_(v)
+        tm.stop(s, "batch")
+    torch.cuda.synchronize()
+    ms = tm.totals()["batch"][0] / (10 * 30)
+    nbytes = 2 * 2 * k.numel() * k.element_size()
+    gbs = nbytes / ms / 1e6
+    return {"us_per_pair": round(ms * 1e3, 3), "bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def spill_commit_row(torch, shape, Cache, k, v):
     """The commit that retires a shot's sink frames from the window (multi-shot sink): with
     S = C = 3 and W = 9, the fourth commit after a shot boundary also moves the shot's first 3
@@ -337,6 +360,7 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     res["commit_30_layers"] = commit_batch_row(torch, shape, Cache, "dense", inputs[0][1], inputs[0][2])
     res["fp4_commit_30_layers"] = commit_batch_row(torch, shape, Cache, "fp4", inputs[0][1], inputs[0][2])
     res["spill_commit_30_layers"] = spill_commit_row(torch, shape, Cache, inputs[0][1], inputs[0][2])
+    res["plain_copy_same_bytes"] = copy_ceiling_row(torch, inputs[0][1], inputs[0][2])
     # FP4 KV store at the layer shape: steady-state attention (15 visible frames)
     c4 = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
                shape.window_frames, kv_format="fp4")

@@ -312,7 +312,10 @@ int launch_scatter(const ScatterArgs& a, void* stream, char* err) {
     const int32_t n_units = min(rows_per_launch, n_rows - r0) * units;
     if (a.fp4) {
       const int blocks = (n_units / units + kFp4Rows - 1) / kFp4Rows;
-      hipLaunchKernelGGL(scatter_fp4_kernel, dim3(blocks, 2), dim3(256), 0, s, p, n_units, units,
+      // as many threads as the workgroup's rows have 64-element units (whole waves, at most
+      // 256): 12 heads x 128 -> 8 rows x 24 units = 192 threads, none idle
+      const int fp4_threads = min(256, (kFp4Rows * units + 63) / 64 * 64);
+      hipLaunchKernelGGL(scatter_fp4_kernel, dim3(blocks, 2), dim3(fp4_threads), 0, s, p, n_units, units,
                          1.0f / float(units), inv_t, gph == 2 ? 1 : 0);
     } else {
       const int blocks = n_units / units;
