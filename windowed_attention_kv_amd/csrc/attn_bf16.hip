@@ -1072,7 +1072,7 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
       // overlapped) and its publish (a spare workgroup runs at most ceil(span/tail) + 1
       // pieces), and kMergeCost per piece the merging workgroup reads. Measured on MI355X:
       // 12 heads x 4680 rows (228 blocks) is faster whole, 1-6 heads are faster split.
-      constexpr int64_t kPieceCost = 5, kMergeCost = 1;
+      constexpr int64_t kPieceCost = 4, kMergeCost = 1;
       const int nt = (p.a.n + TR - 1) / TR + (p.b.n + TR - 1) / TR;
       const int64_t spare = a.n_cu - blocks;
       int best_main = nt;
