@@ -505,8 +505,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
-              "multi-GPU path; the per-head sharding design is described in DESIGN.md",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path; the hot path shards by head with no communication inside it",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -49,7 +49,7 @@ typedef enum {
   LL_OK = 0,
   LL_EINVAL = 1,       /* bad argument: null/misaligned pointer, out-of-range size or layer */
   LL_ESTATE = 2,       /* call not valid in the current cache state (e.g. recache of an empty layer) */
-  LL_EUNSUPPORTED = 3, /* valid request this build does not implement (head_dim, dtype/format mix) */
+  LL_EUNSUPPORTED = 3, /* valid request the library does not implement (head_dim, dtype/format mix) */
   LL_EDEVICE = 4       /* the HIP runtime reported an error (launch failure, no device) */
 } ll_status;
 

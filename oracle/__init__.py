@@ -26,8 +26,7 @@ Sources (pages, by title and section):
   [OCP]  OCP Microscaling Formats (MX) v1.0 specification: FP4 E2M1 element and E8M0 scale
          encodings (an external published definition; the pages only say "FP4")
 
-Readings where the pages are silent are listed in the design doc; each function states the one it
-takes. Parity pins: every function here is checked by `tests/test_oracle_*.py` against
+Where the pages are silent, each function states the reading it takes. Parity pins: every function here is checked by `tests/test_oracle_*.py` against
 brute force, library routines (torch CPU fp64 scaled_dot_product_attention), closed forms
 and invariants. No function in this package is "parity unpinned".
 """

@@ -4,7 +4,8 @@
 can be stored in FP4 with a fused dequant kernel. The element and scale encodings follow
 [OCP] (FP4 E2M1: values 0, 0.5, 1, 1.5, 2, 3, 4, 6 with a sign bit; E8M0: 2^(byte-127)).
 
-Steps for one block of 16 bf16 values x_0..x_15 (readings in the design doc):
+Steps for one block of 16 bf16 values x_0..x_15 (the readings taken where the pages are silent:
+the OCP MX shared-exponent rule, ties to the even code, the sign copied, saturation at 6):
   1. a = max |x_i|; b = the biased exponent field of a (0 for zero and subnormals)
   2. scale byte sb = max(b - 2, 0), i.e. floor(log2 a) - 2 (2 = emax of e2m1) clamped to
      the e8m0 range; E = sb - 127. 0xFF is never produced.

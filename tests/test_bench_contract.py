@@ -1,0 +1,15 @@
+"""CPU checks of bench.py's command-line contract (no GPU needed): more than one GPU is refused
+with a message and a non-zero exit status, before anything touches a device."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+    assert r.stdout == ""

@@ -267,8 +267,13 @@ ll_status ll_cache_create(const ll_cache_desc* desc, void* device_mem, size_t de
                                        : float(1.0 / std::sqrt(double(desc->head_dim)));
   c->n_cu = n_cu;
   c->ws_ready = false;
-  c->frames.assign(size_t(desc->num_layers), 0);
-  c->shot.assign(size_t(desc->num_layers), 0);
+  try {
+    c->frames.assign(size_t(desc->num_layers), 0);
+    c->shot.assign(size_t(desc->num_layers), 0);
+  } catch (...) {  // no exception crosses the C ABI
+    delete c;
+    return fail(LL_EINVAL, "out of host memory");
+  }
   *out = c;
   return ok();
 }
