@@ -115,6 +115,27 @@ def test_fp32_head_dim_128_and_sink_variants():
     run_stream(shape, 7)
 
 
+@pytest.mark.parametrize("case", [
+    # name, base, overrides, kv_format, chunks
+    ("no-sink", "layer", dict(heads=2, tokens_per_frame=20, sink_frames=0, window_frames=3), "dense", 6),
+    ("window-equals-chunk", "layer", dict(heads=1, tokens_per_frame=40, window_frames=3), "dense", 6),
+    ("one-frame-chunks-d64", "layer", dict(heads=2, head_dim=64, tokens_per_frame=30, chunk_frames=1,
+                                           sink_frames=1, window_frames=2), "dense", 8),
+    ("one-token-frames", "layer", dict(heads=2, tokens_per_frame=1, window_frames=6), "dense", 10),
+    ("fp4-no-sink", "layer", dict(heads=2, tokens_per_frame=24, chunk_frames=2, sink_frames=0,
+                                  window_frames=4), "fp4", 7),
+    ("fp32-window-one", "tiny", dict(chunk_frames=1, sink_frames=0, window_frames=1), "dense", 5),
+], ids=lambda c: c[0])
+def test_degenerate_geometries(case):
+    """No sink, a window of exactly one chunk, one-frame chunks, one token per frame (3 query
+    rows, a few keys: every tile mostly masked), FP4 without a sink, an fp32 window of one
+    frame: every chunk compared, cache export bit-exact."""
+    name, base, over, kv_format, chunks = case
+    shape = synth.shrink(synth.CONFIGS[base], name=name, **over)
+    log(f"case: degenerate geometry {name} ({kv_format})")
+    run_stream(shape, chunks, kv_format=kv_format)
+
+
 def test_layer_config_sampled():
     """The 1.3B-DiT-shaped layer: 12 heads x 128, 1560 tokens/frame, chunk 3, sink 3, window 9,
     20 chunks; sampled query rows on fill-up, first wrap and the last chunk."""
