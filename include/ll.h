@@ -157,7 +157,10 @@ ll_status ll_recache(ll_cache* cache, int32_t layer, const void* q, const void* 
                      const void* v, const void* qx, const void* k_text, const void* v_text,
                      int32_t n_text, void* o, void* ox, void* stream);
 
-/* Standalone FP4 codec: x ([rows, row_len] bf16, row_len % 16 == 0) ->
+/* Standalone FP4 codec ("LongLive 2.0" distributed-inference page, section on NVFP4 and KV
+ * cache compression: the KV cache stored in FP4; the e2m1 element and e8m0 scale encodings
+ * and the shared-exponent rule are those of the OCP Microscaling Formats v1.0 spec, the pages
+ * naming only "FP4"). x ([rows, row_len] bf16, row_len % 16 == 0) ->
  * packed [rows, row_len/2] bytes and scales [rows, row_len/16] e8m0 bytes. Per block of 16:
  * scale byte = max(exponent_field(max|x|) - 2, 0); codes = |x| * 2^-(scale-127) rounded to
  * {0,.5,1,1.5,2,3,4,6}, ties to the even code, saturating at 6; sign bit copied. Inputs
