@@ -773,18 +773,18 @@ void attn_bf16_direct_kernel(Params p) {
       const int r0 = (inA ? t : t - ntA) * TR + u2 * BN;       // first row of the sub-tile
       const int seg_left = (inA ? na : nb) - r0;
       // a sub-tile wholly past the end is skipped (FP4: computed fully masked instead, so the
-      // dequantisation below stays in one basic block with the QK products)
+      // last sub-tile always reaches the dequantising store of the next tile)
       if (!FP4 && seg_left <= 0) continue;
       const int key0 = (inA ? 0 : na) + r0;
 
       // S^T = K Q^T: 16 MFMAs, each fed by one 16-byte LDS read. The reads run kPipe MFMAs
       // ahead of their use (pinned by the scheduling groups below), so the LDS latency hides
       // behind the matrix pipe instead of stalling every MFMA.
-      // Wave priority (dense tiles): raised for the MFMA blocks, lowered for the softmax, so
-      // that of the two waves sharing a SIMD the one with MFMAs to issue wins and the other's
-      // VALU work fills the matrix pipe's shadow; that pulls the pair out of phase. (FP4
-      // tiles, whose dequantisation sits in the QK block, run slower with it.)
-      if constexpr (!FP4) __builtin_amdgcn_s_setprio(1);
+      // Wave priority: raised for the MFMA blocks, lowered for the softmax (and the FP4
+      // dequantisation), so that of the two waves sharing a SIMD the one with MFMAs to issue
+      // wins and the other's VALU work fills the matrix pipe's shadow; that pulls the pair
+      // out of phase.
+      __builtin_amdgcn_s_setprio(1);
       f32x16_t s[2];
       s[0] = f32x16_t{};
       s[1] = f32x16_t{};
@@ -806,16 +806,6 @@ void attn_bf16_direct_kernel(Params p) {
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPipe, 0);
       }
-      if constexpr (FP4) {
-        // next tile's FP4 data -> bf16 while the QK products run; when the next tile is not
-        // FP4 (or past the piece) the stores go to a 16 KB scratch area above the two
-        // buffers instead (K and V rows folded onto 64 rows), so no branch is needed
-        if (u2 == SUB - 1) {
-          const bool real = fp4a && t + 1 < t1 && t + 1 < ntA;
-          dequant_store(real ? smem + ((t + 1) & 1) * DT_BUF : smem + 2 * DT_BUF,
-                        real ? DT_TILE : 0, real ? TR - 1 : BN - 1);
-        }
-      }
 
       // mask: rows past the segment's end, and keys past this row's block-causal limit
       if (seg_left < BN || key0 + BN > wave_min_lim) {
@@ -829,9 +819,19 @@ void attn_bf16_direct_kernel(Params p) {
       }
 
       bf16x8_t pb[2][2];
-      if constexpr (!FP4) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
       softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
-      if constexpr (!FP4) __builtin_amdgcn_s_setprio(1);
+      if constexpr (FP4) {
+        // next tile's FP4 data -> bf16 at low priority, next to the softmax; when the next
+        // tile is not FP4 (or past the piece) the stores go to a 16 KB scratch area above the
+        // two buffers instead (K and V rows folded onto 64 rows), so no branch is needed
+        if (u2 == SUB - 1) {
+          const bool real = fp4a && t + 1 < t1 && t + 1 < ntA;
+          dequant_store(real ? smem + ((t + 1) & 1) * DT_BUF : smem + 2 * DT_BUF,
+                        real ? DT_TILE : 0, real ? TR - 1 : BN - 1);
+        }
+      }
+      __builtin_amdgcn_s_setprio(1);
 
       // O^T += V^T P^T: 16 MFMAs, each fed by two transposing LDS reads, pipelined like S
       {
@@ -858,7 +858,7 @@ void attn_bf16_direct_kernel(Params p) {
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPipe, 0);
       }
-      if constexpr (!FP4) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
       }
 
       __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of tile t+1 have landed
