@@ -50,14 +50,25 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
 
 
+def code_hash(path):
+    """sha256 prefix of a C++/HIP source with its comments and whitespace removed: it changes
+    with the code, not with the commentary."""
+    import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode("utf-8")).hexdigest()[:16]
+
+
 def counter_traffic(avg_flops_per_launch):
     """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE summary, but only
-    while the kernel source is the one the counters were taken on (else None)."""
-    import hashlib
+    while the kernel code is the one the counters were taken on (else None)."""
     src = os.path.join(ROOT, "windowed_attention_kv_amd", "csrc", "attn_bf16.hip")
     prof = os.path.join(ROOT, "profiles", "attn_commit_traffic_counters.md")
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = code_hash(src)
         kv = {}
         for line in open(prof):
             if ":" in line and line.startswith("    "):

@@ -23,7 +23,11 @@
 //  * workgroups are mapped so that each XCD (own L2) works on a contiguous range of
 //    (head, query block) tiles: the query blocks of one head share their K/V in one L2;
 //    block-causal (recache) launches instead dispatch the heaviest block rank of every head
-//    first, longest job first over the whole grid.
+//    first, longest job first over the whole grid;
+//  * each MFMA operand is read from LDS four MFMAs ahead of its use (scheduling groups), and
+//    the wave priority is raised for the MFMA blocks and lowered for the softmax, so of the
+//    two waves sharing a SIMD the one with MFMAs to issue wins and the other's VALU work runs
+//    in the matrix pipe's shadow.
 // Two kernels: attn_bf16_direct_kernel (head_dim 128: 8 waves, 128-key tiles loaded straight
 // into LDS, V read with transposing LDS reads, optional split schedule for calls with fewer
 // query blocks than CUs) and attn_bf16_kernel (head_dim 64: 4 waves, 64-key tiles staged
