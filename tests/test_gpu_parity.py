@@ -240,6 +240,26 @@ def test_kv_quant_random_and_ragged_rows():
         wp, ws = ofp4.quantize(x.bits)
         np.testing.assert_array_equal(pk.cpu().numpy(), wp)
         np.testing.assert_array_equal(sc.cpu().numpy(), ws)
+        # caller-supplied outputs are written in place
+        pk2 = torch.empty_like(pk)
+        sc2 = torch.empty_like(sc)
+        kv_quant(t, pk2, sc2)
+        assert torch.equal(pk2, pk) and torch.equal(sc2, sc)
+
+
+def test_kv_quant_rejects_wrong_outputs():
+    """Output buffers that the kernel would overrun are refused before any launch."""
+    import pytest
+    import torch
+    from windowed_attention_kv_amd import kv_quant
+    t = torch.zeros((8, 32), dtype=torch.bfloat16, device="cuda")
+    good_p = torch.empty((8, 16), dtype=torch.uint8, device="cuda")
+    good_s = torch.empty((8, 2), dtype=torch.uint8, device="cuda")
+    for p, s in ((good_p[:7], good_s), (good_p, good_s[:, :1]),
+                 (good_p.to(torch.int8), good_s), (good_p, good_s.cpu())):
+        with pytest.raises(ValueError):
+            kv_quant(t, p, s)
+    assert all(int(b) == 0 for b in kv_quant(t, good_p, good_s)[0].flatten()[:4])
 
 
 def test_fp4_stream():

@@ -191,12 +191,18 @@ def kv_quant(x, packed=None, scales=None):
     torch = _torch()
     if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("kv_quant expects a contiguous bf16 CUDA tensor")
-    L = x.shape[-1]
+    L = x.shape[-1] if x.dim() else 0
     rows = x.numel() // L if L else 0
     if packed is None:
         packed = torch.empty((rows, L // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, L // 16), dtype=torch.uint8, device=x.device)
+    # caller-supplied outputs are written in full by the kernel: check them before the launch
+    for name, t, width in (("packed", packed, L // 2), ("scales", scales, L // 16)):
+        if t.dtype != torch.uint8 or t.device != x.device or not t.is_contiguous() \
+                or t.numel() != rows * width:
+            raise ValueError(f"kv_quant: {name} must be a contiguous uint8 tensor on {x.device} "
+                             f"with {rows * width} elements")
     l = lib()
     check(l, l.ll_kv_quant(ctypes.c_void_p(x.data_ptr()), rows, L,
                            ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
