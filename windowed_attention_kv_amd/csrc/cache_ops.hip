@@ -74,7 +74,7 @@ __device__ __forceinline__ void quant64(const uint8_t* src, uint4& pk0, uint4& p
 
 struct ScatterP {
   int32_t row0;              // first token row of this launch (launches are split below 2^24 units)
-  int32_t ring0;             // (frame - S) mod W of the first non-lead frame
+  int32_t ring0;             // window slot (frame id mod W) of the first non-lead frame
   float inv_w;               // 1 / W
   const uint8_t* src[2];
   uint8_t* dst[2];
@@ -94,7 +94,8 @@ __device__ __forceinline__ int32_t fdiv(int32_t i, int32_t d, float inv) {
   return q;
 }
 
-// Slot of source frame rank r: lead (sink) frames first, then the window ring.
+// Slot of source frame rank r: the lead ranks (spilled sink frames of a recache rewrite) go to
+// consecutive sink slots, the rest to the window ring.
 __device__ __forceinline__ int32_t slot_of_rank(const ScatterP& p, int32_t r) {
   if (r < p.n_lead) return p.lead_slot0 + r;
   const int32_t k = p.ring0 + (r - p.n_lead);

@@ -2,12 +2,12 @@
 // kernel launch plumbing. Nothing here touches device memory; every device operation is an
 // enqueue through launch.h.
 //
-// Cache model ("LongLive" summary page, 方法 §3 高效长推理): each layer holds S sink slots
-// (frames 0..S-1, pinned for good) and W window slots that rotate, so its size depends only
-// on S + W. Frame f sits in slot f (f < S) or S + (f - S) mod W. With F frames committed the
-// held frames are {f < min(F,S)} U [max(S, F-W), F) and the filled slots are always the prefix
-// [0, min(F,S) + min(max(F-S,0), W)), which is what lets one attention kernel read the cache
-// as a single contiguous key range per head.
+// Cache model ("LongLive" summary page, 方法 §3 高效长推理): each layer holds W window slots
+// that rotate and S sink slots after them, so its size depends only on S + W. Frame f enters
+// window slot f mod W; a sink frame of the current shot moves to its sink slot when the
+// window evicts it (slot rules at n_spilled below). The held frames always fill a slot prefix,
+// which is what lets one attention kernel read the cache as a single contiguous key range per
+// head.
 //
 // Device memory layout (per layer, K then V; each plane 256-byte aligned):
 //   dense: [H][(S+W)*T][D] elements of the dtype (head-major, so one head's keys are contiguous)
