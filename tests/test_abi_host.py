@@ -261,6 +261,28 @@ def test_descriptor_validation(fake):
                                 ctypes.byref(h)) == _lib.LL_EINVAL
 
 
+def test_size_limits(fake):
+    """The kernels address a K/V plane with 32-bit byte offsets: (S+W)*T*H*D*2 must stay below
+    2^31 (the bf16 row width bounds FP4 caches too, whose own chunk stays bf16), and a layer
+    holds at most 4096 frame slots. Just under each limit is accepted, at it rejected."""
+    size = ctypes.c_size_t()
+    ok = make_desc(1, 2, 128, 4095, 1, 1, 1023)            # 2,146,959,360 bytes per plane
+    assert fake.ll_cache_size(ctypes.byref(ok), ctypes.byref(size)) == 0
+    assert size.value >= 2 * 1024 * 4095 * 2 * 128 * 2
+    for fmt in ("dense", "fp4"):
+        over = make_desc(1, 2, 128, 4096, 1, 1, 1023, kv_format=fmt)   # exactly 2^31
+        assert fake.ll_cache_size(ctypes.byref(over), ctypes.byref(size)) == _lib.LL_EUNSUPPORTED
+        assert b"2 GiB" in fake.ll_last_error()
+    f32 = make_desc(1, 2, 128, 2047, 1, 1, 1023, dtype="f32")          # 4-byte elements
+    assert fake.ll_cache_size(ctypes.byref(f32), ctypes.byref(size)) == 0
+    f32.tokens_per_frame = 2048
+    assert fake.ll_cache_size(ctypes.byref(f32), ctypes.byref(size)) == _lib.LL_EUNSUPPORTED
+    assert fake.ll_cache_size(ctypes.byref(make_desc(1, 1, 64, 1, 1, 0, 4096)),
+                              ctypes.byref(size)) == 0
+    assert fake.ll_cache_size(ctypes.byref(make_desc(1, 1, 64, 1, 1, 1, 4096)),
+                              ctypes.byref(size)) == _lib.LL_EINVAL
+
+
 def _split_workspace(H, n, cache_keys, n_cu):
     """Workspace of the split attention schedule (dense bf16, head_dim 128): one 32-bit
     counter per (head, 256-row query block), padded to 256 bytes, then two slots of

@@ -512,3 +512,47 @@ def test_stack_config_sampled():
             assert torch.equal(K[slot * T:(slot + 1) * T], tk[i * T:(i + 1) * T]), (layer, slot, f)
             assert torch.equal(V[slot * T:(slot + 1) * T], tv[i * T:(i + 1) * T]), (layer, slot, f)
 
+
+
+@pytest.mark.parametrize("kv_format", ["dense", "fp4"])
+def test_cache_at_the_size_limit(kv_format):
+    """The largest cache the library accepts at 2 heads x 128 in bf16: (S+W)*T*H*D*2 =
+    2,146,959,360 bytes per K/V plane, just under the 2^31 bound of the kernels' 32-bit byte
+    offsets (S=1, W=1023, T=4095, C=1; 4.19M keys per head). All T tokens of a frame carry
+    the same K and V rows, and every visible frame has T tokens, so attention over the cache
+    equals attention over one key per visible frame: the oracle computes every output row from
+    the frame vectors. Checked with the cache partly filled, and after the window has wrapped
+    and the sink frame has moved to its sink slot."""
+    import torch
+    from windowed_attention_kv_amd import Cache
+    H, D, T, C, S, W = 2, 128, 4095, 1, 1, 1023
+    assert (S + W) * T * H * D * 2 < 2 ** 31 <= (S + W) * (T + 1) * H * D * 2
+    n_frames = W + S + 5
+    kf = synth.draw((n_frames, H, D), "bf16", 1.0, synth.rng(60, 0, 0, 0, 1))
+    vf = synth.draw((n_frames, H, D), "bf16", 0.5, synth.rng(60, 0, 0, 0, 2))
+    tkf, tvf = kf.torch("cuda"), vf.torch("cuda")
+
+    def frame(t, f):
+        return t[f].expand(T, H, D).contiguous()
+
+    def held(x, f):
+        """What the cache holds for committed frame f (one token row, float64)."""
+        return ofp4.roundtrip(x.bits[f]) if kv_format == "fp4" else x.values[f].astype(np.float64)
+
+    cache = Cache(1, H, D, T, C, S, W, kv_format=kv_format)
+    for c in range(n_frames):
+        if c in (600, n_frames - 1):
+            log(f"case: cache at the size limit, {kv_format}, chunk {c}")
+            q = synth.draw((T, H, D), "bf16", 1.0, synth.rng(60, 0, 0, c, 0))
+            o = cache.attn_chunk(0, q.torch("cuda"), frame(tkf, c), frame(tvf, c))
+            vis = ring.visible_frames(c, C, S, W)
+            K = np.stack([held(kf, f) if f < c else kf.values[f] for f in vis])
+            V = np.stack([held(vf, f) if f < c else vf.values[f] for f in vis])
+            ref = oatt.attention(q.values, K, V, 1.0 / math.sqrt(D))
+            ma, rl = assert_close(to_np(o), ref, "bf16", f"size limit {kv_format} chunk {c}")
+            log(f"size limit {kv_format} chunk {c}: max-abs {ma:.3e} rel-L2 {rl:.3e}")
+        cache.commit(0, frame(tkf, c), frame(tvf, c))
+    F, slots = cache.state(0)
+    assert F == n_frames and slots == ring.slot_map(F, S, W)
+    del cache
+    torch.cuda.empty_cache()
