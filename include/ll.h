@@ -63,8 +63,8 @@ typedef enum { LL_KV_DENSE = 0, LL_KV_FP4 = 1 } ll_kv_format;
 
 typedef struct {
   uint32_t abi_version;    /* must be LL_ABI_VERSION */
-  int32_t num_layers;      /* >= 1 */
-  int32_t num_heads;       /* H >= 1 */
+  int32_t num_layers;      /* 1..4096 */
+  int32_t num_heads;       /* H: 1..1024 */
   int32_t head_dim;        /* D: 64 or 128 */
   int32_t tokens_per_frame;/* T >= 1 */
   int32_t chunk_frames;    /* C >= 1: frames produced (and committed) per chunk; C <= W */
@@ -85,7 +85,10 @@ typedef struct ll_cache ll_cache; /* opaque host handle */
  * 2 * min(CUs, blocks * tiles) slots of 135,168 bytes, with tiles = ceil((S+W)*T/128) +
  * ceil(C*T/128). The CU count is that of the device current at the call, so create the
  * cache with the same device current. Fails with LL_EINVAL / LL_EUNSUPPORTED on a bad
- * descriptor. */
+ * descriptor. Size limits (the kernels use 32-bit byte offsets within a K or V plane):
+ * (S+W)*T*H*D times the dtype's element size must stay below 2^31 bytes (FP4 caches are held
+ * to the bf16 bound, since the own chunk stays bf16), else LL_EUNSUPPORTED; S+W <= 4096
+ * slots, else LL_EINVAL. */
 ll_status ll_cache_size(const ll_cache_desc* desc, size_t* device_bytes);
 
 /* Create a handle over caller-owned device memory `device_mem` (256-byte aligned, at least
