@@ -14,9 +14,10 @@
 //    max / row sum are in-lane reductions plus one v_permlane32_swap, never a cross-lane tree;
 //  * P^T goes straight from the S accumulator into the B operand of O^T = V^T P^T (no LDS
 //    round trip);
-//  * online softmax in the exp2 domain with a lazy rescale: the running max only moves when a
-//    tile's max exceeds it by more than 2^8, so the O rescale (64 multiplies per lane) is
-//    rare; softmax is shift-invariant, so this changes rounding only;
+//  * online softmax in the exp2 domain with a lazy rescale: a tile's weights are taken against
+//    the running max as it stands, and only when a lane's weights sum to more than 2^8 does
+//    the wave compute the tile max, rescale O (64 multiplies per lane) and redo the weights;
+//    softmax is shift-invariant, so this changes rounding only;
 //  * FP4 cache tiles are dequantised exactly while being written to LDS, so the MFMA inner
 //    loop is identical for both cache formats ("LongLive 2.0" distributed-inference page,
 //    NVFP4 and KV cache section: fused dequantisation);
@@ -48,7 +49,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;          // keys per tile
-constexpr float kLazyRescale = 8.0f;  // log2 of the largest allowed p before a rescale
+constexpr float kLazyBound = 256.0f;   // largest allowed sum of a lane's weights in a tile
+// start of the running max: finite, so that a visible score gives exp2(+huge) = +inf (forcing
+// the first rescale) and a masked one (-inf) gives 0, and no weight or sum is ever NaN
+constexpr float kNoMax = -1e30f;
 
 struct DevSeg {
   const uint8_t* k;   // dense: bf16 base; fp4: packed base
@@ -296,38 +300,22 @@ struct Stage {
 // Online softmax of one 64-key tile for the lane's query row: S^T values s (2 x 16 per lane,
 // masked keys already -inf) -> bf16 weights pb (the B operand of the PV product), updating the
 // running max m (exp2 domain, scaled by c), the running sum l and, when the max moves, O.
-// The running max only moves when the tile max exceeds it by more than 2^8 (lazy rescale:
-// softmax is shift-invariant, so this only changes rounding); the row sum adds the
-// bf16-rounded weights (v_dot2 with ones), exactly the weights the PV product uses.
+// Lazy rescale: the weights are first taken against the running max as it stands. Each is at
+// most the lane's sum of them, so while no lane's sum exceeds 2^8 the tile needs no rescale
+// (softmax is shift-invariant; only rounding changes) and the tile max is never computed.
+// Otherwise (the first tile, or scores well above the running max) the wave takes the tile
+// max, rescales O and l and recomputes the weights. The row sum adds the bf16-rounded weights
+// (v_dot2 with ones), exactly the weights the PV product uses.
 template <int D>
-__device__ __forceinline__ void softmax_update(f32x16_t (&s)[2], float c, float& m_run,
-                                               float& l_run, f32x16_t (&oacc)[D / 32],
-                                               bf16x8_t (&pb)[2][2]) {
-  float t8[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    t8[i] = fmaxf(fmaxf(s[0][2 * i], s[0][2 * i + 1]), fmaxf(s[1][2 * i], s[1][2 * i + 1]));
-#pragma unroll
-  for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-    for (int i = 0; i < w; ++i) t8[i] = fmaxf(t8[i], t8[i + w]);
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t8[0]), __float_as_uint(t8[0]),
-                                                   false, false);
-  const float mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
-  if (mt > m_run + kLazyRescale) {
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
-    l_run *= alpha;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-    m_run = mt;
-  }
+__device__ __forceinline__ float tile_weights(const f32x16_t (&s)[2], float c, float m,
+                                              bf16x8_t (&pb)[2][2]) {
   float psum[4] = {0.f, 0.f, 0.f, 0.f};
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     float e[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_run));
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t u[4];
@@ -339,7 +327,36 @@ __device__ __forceinline__ void softmax_update(f32x16_t (&s)[2], float c, float&
       pb[kb][j] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
     }
   }
-  l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+  return (psum[0] + psum[1]) + (psum[2] + psum[3]);
+}
+
+template <int D>
+__device__ __forceinline__ void softmax_update(f32x16_t (&s)[2], float c, float& m_run,
+                                               float& l_run, f32x16_t (&oacc)[D / 32],
+                                               bf16x8_t (&pb)[2][2]) {
+  float ls = tile_weights<D>(s, c, m_run, pb);
+  if (__builtin_amdgcn_ballot_w64(ls > kLazyBound)) {
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      t8[i] = fmaxf(fmaxf(s[0][2 * i], s[0][2 * i + 1]), fmaxf(s[1][2 * i], s[1][2 * i + 1]));
+#pragma unroll
+    for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) t8[i] = fmaxf(t8[i], t8[i + w]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t8[0]), __float_as_uint(t8[0]),
+                                                     false, false);
+    const float mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+    if (mt > m_run) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+      m_run = mt;
+    }
+    ls = tile_weights<D>(s, c, m_run, pb);
+  }
+  l_run += ls;
 }
 
 template <int D, int NW, bool FP4>
@@ -384,7 +401,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   f32x16_t oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16_t{};
-  float m_run = -__builtin_inff();
+  float m_run = kNoMax;
   float l_run = 0.f;
 
   // per-lane LDS offsets (tile-invariant): K row l32 column hi; V^T row l32 at the four
@@ -701,7 +718,7 @@ void attn_bf16_direct_kernel(Params p) {
     f32x16_t oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16_t{};
-    float m_run = -__builtin_inff();
+    float m_run = kNoMax;
     float l_run = 0.f;
 
     // FP4 cache tiles (segment A under FP4) are staged through registers instead: thread
