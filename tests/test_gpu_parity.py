@@ -101,6 +101,21 @@ def test_bf16_peaked_and_frame_offsets():
     run_stream(shape, 7, peaked=True, v_frame_offset=0.25)
 
 
+@pytest.mark.parametrize("kind", ["bf16-d128", "bf16-d64", "fp4"])
+def test_rising_scores_force_rescales(kind):
+    """K of frame f scaled by 1 + 2f: the keys of later frames give ever larger scores, so a
+    row's largest score keeps jumping while its keys are swept (slot order is not time order,
+    and the own chunk comes last). That drives the kernels' running-max rescale of O and the
+    row sum in the middle of a sweep, not only on its first tile: on these inputs a row's
+    exact running max rises by more than 8 (exp2 domain) within one 64-key step for over 1% of
+    (row, step) pairs (pinned on the CPU in test_oracle_model.py)."""
+    D = 64 if kind == "bf16-d64" else 128
+    shape = synth.shrink(synth.CONFIGS["layer"], name=f"rising-{kind}", heads=2, head_dim=D,
+                         tokens_per_frame=100, window_frames=5)
+    log(f"case: rising scores {kind}")
+    run_stream(shape, 8, kv_format="fp4" if kind == "fp4" else "dense", k_frame_gain=2.0)
+
+
 def test_denoise_steps_only_last_commits():
     shape = synth.shrink(synth.CONFIGS["layer"], name="steps", heads=2, tokens_per_frame=40,
                          window_frames=4)

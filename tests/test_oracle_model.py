@@ -10,6 +10,7 @@ import math
 import numpy as np
 import pytest
 
+from oracle import attention as oatt
 from oracle import fp4, ring
 from oracle.model import LayerModel, bruteforce_chunk
 from windowed_attention_kv_amd import synth
@@ -249,3 +250,31 @@ def test_fp4_store_attends_to_dequantised_history():
                                   d.attn_chunk(q.values, k.values, v.values))
     kp, ks, vp, vs, valid = m.export_fp4()
     assert valid.sum() == 12 * 32 * 2
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_rising_score_inputs_move_the_running_max(D):
+    """The input recipe of the GPU rescale test (K of frame f scaled by 1 + 2f, 2 heads,
+    T = 100, C = 3, S = 3, W = 5, 8 chunks) really moves a row's largest score in the middle of
+    its key sweep: sweeping each chunk's keys in cache slot order and then the own chunk, in
+    64-key steps, the exact running max (exp2 domain) rises by more than 8 within a step for
+    over 1% of (row, step) pairs after the first step. A weight there exceeds 2^8, so any
+    rescale rule with that bound must act mid-sweep."""
+    T, C, S, W = 100, 3, 3, 5
+    shape = synth.shrink(synth.CONFIGS["layer"], name="rising", heads=2, head_dim=D,
+                         tokens_per_frame=T, window_frames=W)
+    keys, steps, jumps = {}, 0, 0
+    for c in range(8):
+        q, k, _ = synth.chunk_inputs(shape, 0, 0, c, k_frame_gain=2.0)
+        for i in range(C):
+            keys[c * C + i] = k.values[i * T:(i + 1) * T]
+        order = [f for f in ring.slot_map(c * C, S, W) if f >= 0] + [c * C + i for i in range(C)]
+        z = oatt.logits(q.values, np.concatenate([keys[f] for f in order]),
+                        1.0 / math.sqrt(D)) * math.log2(math.e)
+        run = np.maximum.accumulate(z, axis=-1)
+        n = z.shape[-1]
+        for t0 in range(64, n, 64):
+            before, after = run[..., t0 - 1], run[..., min(t0 + 63, n - 1)]
+            steps += before.size
+            jumps += int(np.sum(after > before + 8))
+    assert jumps > 0.01 * steps, (jumps, steps)

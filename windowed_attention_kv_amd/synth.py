@@ -101,9 +101,9 @@ class Tensor:
 
 
 def draw(shape_rows: tuple, dtype: str, std: float, gen: np.random.Generator,
-         offset: np.ndarray | float = 0.0) -> Tensor:
+         offset: np.ndarray | float = 0.0, gain: np.ndarray | float = 1.0) -> Tensor:
     x = gen.standard_normal(shape_rows, dtype=np.float32) * np.float32(std)
-    x = (x + np.asarray(offset, dtype=np.float32)).astype(np.float32)
+    x = (x * np.asarray(gain, dtype=np.float32) + np.asarray(offset, dtype=np.float32)).astype(np.float32)
     if dtype == "f32":
         return Tensor(x, None)
     bits = f32_to_bf16_bits(x)
@@ -111,24 +111,27 @@ def draw(shape_rows: tuple, dtype: str, std: float, gen: np.random.Generator,
 
 
 def chunk_inputs(shape: Shape, layer: int, step: int, chunk: int, *, peaked: bool = False,
-                 v_frame_offset: float = 0.0, salt: int = 0):
+                 v_frame_offset: float = 0.0, k_frame_gain: float = 0.0, salt: int = 0):
     """Q, K, V of one chunk, each [C*T, H, D].
 
     peaked: Q and K drawn with twice the std (sharper softmax).
     v_frame_offset: V of frame f gets + f * v_frame_offset, so a wrong or stale frame shows
     up as a large error.
+    k_frame_gain: K of frame f is scaled by 1 + f * k_frame_gain, so later frames give ever
+    larger scores (the largest score of a row keeps moving as its keys are swept).
     """
     rows = (shape.n_query, shape.heads, shape.head_dim)
     std = shape.value_scale * (2.0 if peaked else 1.0)
+    frame = chunk * shape.chunk_frames + np.arange(shape.n_query) // shape.tokens_per_frame
     out = []
     for tid in (Q, K, V):
         g = rng(shape.cfg_id, layer, step, chunk, tid, salt)
-        off = 0.0
+        off, gain = 0.0, 1.0
         if tid == V and v_frame_offset:
-            frame0 = chunk * shape.chunk_frames
-            fr = frame0 + np.arange(shape.n_query) // shape.tokens_per_frame
-            off = (fr * v_frame_offset).astype(np.float32)[:, None, None]
-        out.append(draw(rows, shape.dtype, std if tid != V else shape.value_scale, g, off))
+            off = (frame * v_frame_offset).astype(np.float32)[:, None, None]
+        if tid == K and k_frame_gain:
+            gain = (1.0 + frame * k_frame_gain).astype(np.float32)[:, None, None]
+        out.append(draw(rows, shape.dtype, std if tid != V else shape.value_scale, g, off, gain))
     return tuple(out)
 
 
