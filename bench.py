@@ -145,10 +145,10 @@ _OUT = [None]
 
 
 def cpu_baseline(shape):
-    """The fp64 oracle on a bounded sample of the same workload: the steady-state chunk
-    (full window: 15 frames = 23400 keys) for 2 of the 12 heads and all 4680 rows, scaled
-    by flops to the whole 20-chunk stream."""
-    import numpy as np
+    """The fp64 oracle on a bounded sample of the same workload: the whole 20-chunk stream
+    (fill-up and steady chunks, attention and commit, inputs drawn beforehand) for 2 of the 12
+    heads and all 4680 rows of each chunk, scaled to 12 heads (heads are independent and cost
+    the same)."""
     from oracle.model import LayerModel
     from windowed_attention_kv_amd import synth
     try:
@@ -160,26 +160,18 @@ def cpu_baseline(shape):
     sub = synth.shrink(shape, heads=Hs)
     m = LayerModel(sub.sink_frames, sub.window_frames, sub.chunk_frames, sub.tokens_per_frame,
                    Hs, sub.head_dim)
-    steady = 5
-    for c in range(steady):
-        _, k, v = synth.chunk_inputs(sub, 0, 0, c)
-        m.commit(k.values, v.values)
-    q, k, v = synth.chunk_inputs(sub, 0, 0, steady)
+    inputs = [synth.chunk_inputs(sub, 0, 0, c) for c in range(shape.chunks)]
     t0 = time.perf_counter()
-    m.attn_chunk(q.values, k.values, v.values)
+    for q, k, v in inputs:
+        m.attn_chunk(q.values, k.values, v.values)
+        m.commit(k.values, v.values)
     dt = time.perf_counter() - t0
-    n = shape.n_query
-    keys = visible_keys(steady, shape.chunk_frames, shape.sink_frames, shape.window_frames,
-                        shape.tokens_per_frame)
-    sample_flops = float(n) * keys * Hs * 4 * shape.head_dim
-    stream_flops = sum(float(n) * visible_keys(c, shape.chunk_frames, shape.sink_frames,
-                                               shape.window_frames, shape.tokens_per_frame)
-                       * shape.heads * 4 * shape.head_dim for c in range(shape.chunks))
-    stream_time = dt * stream_flops / sample_flops
-    return {"value": round(n * shape.chunks / stream_time, 3), "unit": "query-tokens/s",
+    stream_time = dt * shape.heads / Hs
+    return {"value": round(shape.n_query * shape.chunks / stream_time, 3), "unit": "query-tokens/s",
             "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 oracle, steady chunk (23400 keys), {Hs}/12 heads x 4680 rows, "
-                       f"{dt:.2f} s measured, scaled by flops to the 20-chunk stream")}
+            "sample": (f"fp64 oracle, the whole {shape.chunks}-chunk stream (attention + commit) "
+                       f"for {Hs}/{shape.heads} heads x {shape.n_query} rows, {dt:.1f} s measured, "
+                       f"scaled by heads to {shape.heads}")}
 
 
 def stack_row(torch, shape, Cache, attn_flops, kv_format, pool):
