@@ -180,6 +180,36 @@ def test_split_with_many_pieces():
     run_stream(shape, 8)
 
 
+def test_side_stream():
+    """Every call enqueues on the caller's stream: a stream run entirely on a side stream
+    (split schedule at 1 head, FP4 store, commits, the first call's counter clearing) while
+    the default stream is kept busy, read back only after that stream is synchronised."""
+    import torch
+    shape = synth.shrink(synth.CONFIGS["layer"], name="side-stream", heads=1,
+                         tokens_per_frame=400, window_frames=6)
+    log("case: side stream, split schedule, FP4")
+    side = torch.cuda.Stream()
+    busy = torch.empty((4096, 4096), device="cuda")
+    with torch.cuda.stream(side):
+        cache = _cache(shape, "fp4")
+    model = _model(shape, "fp4")
+    for c in range(8):
+        q, k, v = synth.chunk_inputs(shape, 0, 0, c)
+        with torch.cuda.stream(side):
+            tq, tk, tv = q.torch("cuda"), k.torch("cuda"), v.torch("cuda")
+        busy.normal_()                                   # default-stream work in between
+        busy = busy @ busy
+        with torch.cuda.stream(side):
+            o = cache.attn_chunk(0, tq, tk, tv)
+            cache.commit(0, tk, tv)
+            o_host = o.to("cpu", non_blocking=False)
+        side.synchronize()
+        ref = model.attn_chunk(q.values, k.values, v.values)
+        assert_close(o_host.to(torch.float64).numpy(), ref, "bf16", f"side stream chunk {c}")
+        model.commit(k.values, v.values, k.bits, v.bits)
+    torch.cuda.synchronize()
+
+
 def test_value_one_gives_one_and_determinism():
     import torch
     shape = synth.shrink(synth.CONFIGS["layer"], heads=2, tokens_per_frame=90, window_frames=4)
