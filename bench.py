@@ -325,6 +325,40 @@ def copy_ceiling_row(torch, k, v):
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def quant_chunk_row(torch, k, v):
+    """Context for the FP4 commit row: ll_kv_quant over exactly the bytes a quantising commit
+    moves (one chunk's K and V: 2 x 14.38 MB of bf16 read, 2 x 4.04 MB of codes and scales
+    written), without the slot scatter; 30 back-to-back launches into 30 output buffers, called
+    through the C ABI with prepared arguments, events bracketing each batch like
+    commit_batch_row."""
+    import ctypes
+    from windowed_attention_kv_amd import _lib
+    lib = _lib.lib()
+    x = torch.cat([k.reshape(-1, k.shape[-1]), v.reshape(-1, v.shape[-1])]).contiguous()
+    rows, D = x.shape
+    outs = [(torch.empty((rows, D // 2), dtype=torch.uint8, device="cuda"),
+             torch.empty((rows, D // 16), dtype=torch.uint8, device="cuda")) for _ in range(30)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = [(ctypes.c_void_p(x.data_ptr()), rows, D, ctypes.c_void_p(pk.data_ptr()),
+             ctypes.c_void_p(sc.data_ptr()), stream) for pk, sc in outs]
+    for a in args[:3]:
+        _lib.check(lib, lib.ll_kv_quant(*a))
+    tm = EventTimer(torch)
+    for rep in range(10):
+        s = tm.start()
+        for a in args:
+            lib.ll_kv_quant(*a)
+        tm.stop(s, "batch")
+    torch.cuda.synchronize()
+    for a in args:
+        _lib.check(lib, lib.ll_kv_quant(*a))
+    ms = tm.totals()["batch"][0] / (10 * 30)
+    nbytes = x.numel() * 2 + outs[0][0].numel() + outs[0][1].numel()
+    gbs = nbytes / ms / 1e6
+    return {"us_per_quant": round(ms * 1e3, 3), "bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def spill_commit_row(torch, shape, Cache, k, v):
     """The commit that retires a shot's sink frames from the window (multi-shot sink): with
     S = C = 3 and W = 9, the fourth commit after a shot boundary also moves the shot's first 3
@@ -364,6 +398,7 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     res["fp4_commit_30_layers"] = commit_batch_row(torch, shape, Cache, "fp4", inputs[0][1], inputs[0][2])
     res["spill_commit_30_layers"] = spill_commit_row(torch, shape, Cache, inputs[0][1], inputs[0][2])
     res["plain_copy_same_bytes"] = copy_ceiling_row(torch, inputs[0][1], inputs[0][2])
+    res["kv_quant_same_bytes_as_fp4_commit"] = quant_chunk_row(torch, inputs[0][1], inputs[0][2])
     # FP4 KV store at the layer shape: steady-state attention (15 visible frames)
     c4 = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
                shape.window_frames, kv_format="fp4")
