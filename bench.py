@@ -461,23 +461,25 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     Hs = 3
     share_in = [tuple(t[:, :Hs].contiguous() for t in trip) for trip in inputs]
     outs = torch.empty((n, Hs, D), dtype=torch.bfloat16, device="cuda")
-    cs = Cache(1, Hs, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
-               shape.window_frames)
-    for rep in range(2):
-        cs.reset()
-        tm = EventTimer(torch)
-        for c, (q, k, v) in enumerate(share_in):
-            s = tm.start()
-            cs.attn_chunk(0, q, k, v, out=outs)
-            tm.stop(s, "attn_steady" if c >= 4 else "attn_fill")
-            cs.commit(0, k, v)
-        torch.cuda.synchronize()
-    tot = tm.totals()
-    ms = tot["attn_steady"][0] / tot["attn_steady"][1]
     share_flops = attn_flops(n, 23400, Hs, D)
-    res["share_3_heads_steady"] = {"ms": round(ms, 4), "tflops": round(share_flops / ms / 1e9, 1),
-                                   "frac_bf16_peak": round(share_flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
-                                   "note": "3 of 12 heads (4-way sequence-parallel share), split schedule"}
+    for kv_format, row in (("dense", "share_3_heads_steady"), ("fp4", "fp4_share_3_heads_steady")):
+        cs = Cache(1, Hs, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
+                   shape.window_frames, kv_format=kv_format)
+        for rep in range(2):
+            cs.reset()
+            tm = EventTimer(torch)
+            for c, (q, k, v) in enumerate(share_in):
+                s = tm.start()
+                cs.attn_chunk(0, q, k, v, out=outs)
+                tm.stop(s, "attn_steady" if c >= 4 else "attn_fill")
+                cs.commit(0, k, v)
+            torch.cuda.synchronize()
+        tot = tm.totals()
+        ms = tot["attn_steady"][0] / tot["attn_steady"][1]
+        res[row] = {"ms": round(ms, 4), "tflops": round(share_flops / ms / 1e9, 1),
+                    "frac_bf16_peak": round(share_flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "note": (f"3 of 12 heads (4-way sequence-parallel share), {kv_format} cache, "
+                             "split schedule")}
     del share_in, outs, cs
     # standalone quant of one 12-frame cache (K and V): 2 x 18720 x 1536 elements
     x = torch.randn((2 * 18720 * H, D), device="cuda").mul_(0.5).to(torch.bfloat16)

@@ -160,14 +160,16 @@ def test_layer_config_sampled():
     run_stream(shape, 20, compare={0, 1, 3, 4, 5, 19}, rows=rows, export_every=False)
 
 
-def test_three_head_share_sampled():
+@pytest.mark.parametrize("kv_format", ["dense", "fp4"])
+def test_three_head_share_sampled(kv_format):
     """The layer shape at 3 heads (one GPU's share of 12 heads over 4 sequence-parallel
     ranks): 57 query blocks on a 256-CU device, so chunk attention runs split into equal key
-    ranges with up to 6 pieces per block that are merged on the device."""
+    ranges with up to 6 pieces per block that are merged on the device; dense and FP4 stores."""
     shape = synth.shrink(synth.CONFIGS["layer"], name="share-h3", heads=3)
-    log("case: layer config at 3 heads, 8 chunks, sampled rows")
+    log(f"case: layer config at 3 heads, {kv_format}, 8 chunks, sampled rows")
     rows = sample_rows(shape.n_query, 64, seed=3)
-    run_stream(shape, 8, compare={0, 2, 4, 5, 7}, rows=rows, export_every=False)
+    run_stream(shape, 8, kv_format=kv_format, compare={0, 2, 4, 5, 7}, rows=rows,
+               export_every=False)
 
 
 def test_split_with_many_pieces():

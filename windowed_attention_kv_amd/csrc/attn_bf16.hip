@@ -918,30 +918,40 @@ void attn_bf16_direct_kernel(Params p) {
       __syncthreads();
       if (!s_last) continue;
       // merge: the main piece, then the tail pieces in range order (the result does not
-      // depend on which workgroup merges)
-      // Reads use buffer loads with the agent-scope (sc1) cache policy, the encoding of an
-      // agent-scope atomic load; as plain loads they may be issued back to back. Pass 1
-      // takes the largest running max, pass 2 sums the rescaled pieces.
+      // depend on which workgroup merges), online: the sum is rescaled whenever a piece brings
+      // a larger running max. Reads use buffer loads with the agent-scope (sc1) cache policy,
+      // the encoding of an agent-scope atomic load; as plain loads they may be issued back to
+      // back. A piece's 66 values are loaded into registers before any is used (scheduling
+      // barrier): left to itself, the compiler waited after every load in the FP4
+      // instantiation, whose registers run at the limit, and a merge of many pieces then took
+      // hundreds of microseconds.
       const __amdgpu_buffer_rsrc_t rpart = rsrc(p.part, 0xFFFFFFFFu);
-      auto slot_of_piece = [&](int gs) { return gs < gs_first ? blk : nblk + gs + blk; };
-      auto ld = [&](int sl, int r) {
-        const uint32_t off = uint32_t((int64_t(sl) * SS::SLOT_FLOATS + r * NW * 64 + wave * 64 + lane) * 4);
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, off, 0, 16));
-      };
-      float m_all = -__builtin_inff();
-      for (int gs = gs_first - 1; gs <= gs_last; ++gs) m_all = fmaxf(m_all, ld(slot_of_piece(gs), 64));
+      float m_all = kNoMax;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16_t{};
       l_run = 0.f;
       for (int gs = gs_first - 1; gs <= gs_last; ++gs) {
-        const int sl = slot_of_piece(gs);
-        const float m_p = ld(sl, 64);
+        const int sl = gs < gs_first ? blk : nblk + gs + blk;
+        const uint32_t base = uint32_t((int64_t(sl) * SS::SLOT_FLOATS + wave * 64 + lane) * 4);
+        float b[SS::REGS];
+#pragma unroll
+        for (int r = 0; r < SS::REGS; ++r)
+          b[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, base + r * NW * 64 * 4, 0, 16));
+        __builtin_amdgcn_sched_barrier(0);
+        const float m_p = b[64];
+        if (m_p > m_all) {   // this piece raises the lane's running max: rescale the sum
+          const float a = __builtin_amdgcn_exp2f(m_all - m_p);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) oacc[db] *= a;
+          l_run *= a;
+          m_all = m_p;
+        }
         const float f = m_p == m_all ? 1.0f : __builtin_amdgcn_exp2f(m_p - m_all);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] += ld(sl, db * 16 + i) * f;
-        l_run += ld(sl, 65) * f;
+          for (int i = 0; i < 16; ++i) oacc[db][i] += b[db * 16 + i] * f;
+        l_run += b[65] * f;
       }
       m_run = m_all;
     }
