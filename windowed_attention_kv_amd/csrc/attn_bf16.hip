@@ -509,6 +509,9 @@ constexpr int DT_ROW = 256;                 // bytes per key row (128 bf16)
 // the AMDGPU backend (MFMA, LDS read)
 constexpr int kPipe = 4;
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+// s_waitcnt immediate for vmcnt <= 4 with expcnt and lgkmcnt at 0 (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8)
+constexpr int kWaitVm4 = 0x0004;
 
 // LDS plan of the direct kernel: SUB 64-key sub-tiles per barrier, K then V, double-buffered
 template <int SUB>
@@ -723,44 +726,54 @@ void attn_bf16_direct_kernel(Params p) {
 
     // FP4 cache tiles (segment A under FP4) are staged through registers instead: thread
     // tid holds row tid/4, elements 32*(tid%4).. of the tile -- 16 packed bytes and 2 scale
-    // bytes per tensor -- and dequant_store() writes them as bf16 into the same swizzled
-    // layout the direct loads produce.
+    // bytes per tensor -- and dequant_half() writes K or V as bf16 into the same swizzled
+    // layout the direct loads produce. The loads of an FP4 tile go out a whole tile ahead of
+    // its dequantisation (load_fp4), so the conversions find their data in registers.
     uint4 kq = make_uint4(0, 0, 0, 0), vq = make_uint4(0, 0, 0, 0);
     uint32_t kqs = 0, vqs = 0;
     const int fr = tid >> 2, fq = tid & 3;
-    auto dequant_store = [&](uint8_t* buf, int v_off, int row_mask) {
-      const int rsw_k = fr & 15, rsw_v = (fr & 3) << 2;
-      const int wr = fr & row_mask;
-      const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w}, vw[4] = {vq.x, vq.y, vq.z, vq.w};
+    auto fp4_tile = [&](int t) { return fp4a && t < ntA; };
+    auto dequant_half = [&](uint8_t* buf, int v_off, int row_mask, bool k_half) {
+      const int rsw = k_half ? (fr & 15) : ((fr & 3) << 2);
+      const uint4 q4 = k_half ? kq : vq;
+      const uint32_t qs = k_half ? kqs : vqs;
+      const uint32_t w[4] = {q4.x, q4.y, q4.z, q4.w};
+      uint8_t* dst = buf + (k_half ? 0 : v_off) + (fr & row_mask) * DT_ROW;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int lc = 4 * fq + c;                            // logical 16-byte chunk (8 elements)
-        const uint4 kd = dequant8(kw[c], (kqs >> (8 * (c >> 1))) & 0xFF);
-        const uint4 vd = dequant8(vw[c], (vqs >> (8 * (c >> 1))) & 0xFF);
-        *reinterpret_cast<uint4*>(buf + wr * DT_ROW + ((lc ^ rsw_k) << 4)) = kd;
-        *reinterpret_cast<uint4*>(buf + v_off + wr * DT_ROW + ((lc ^ rsw_v) << 4)) = vd;
+        *reinterpret_cast<uint4*>(dst + ((lc ^ rsw) << 4)) = dequant8(w[c], (qs >> (8 * (c >> 1))) & 0xFF);
       }
+    };
+    auto load_fp4 = [&](int t, bool k_half) {
+      const int r0 = t * TR;
+      const int64_t e0 = h * p.a.head_stride + int64_t(r0) * p.a.row_stride;
+      const int left = p.a.n - r0;
+      const uint32_t pbytes = left > 0 ? uint32_t(left) * (D / 2) : 0u;
+      const __amdgpu_buffer_rsrc_t rc = rsrc((k_half ? p.a.k : p.a.v) + e0 / 2, pbytes);
+      const __amdgpu_buffer_rsrc_t rs = rsrc((k_half ? p.a.ks : p.a.vs) + e0 / 16, pbytes / 8);
+      const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, uint32_t(fr) * (D / 2) + fq * 16, 0, 0));
+      const uint32_t s = __builtin_amdgcn_raw_buffer_load_b16(rs, uint32_t(fr) * (D / 16) + fq * 2, 0, 0);
+      if (k_half) {
+        kq = x;
+        kqs = s;
+      } else {
+        vq = x;
+        vqs = s;
+      }
+    };
+    // wait for this wave's direct loads of the next tile; when the FP4 loads of the tile after
+    // it are already in flight (only possible with no direct load outstanding: FP4 tiles come
+    // first) they are the last 4 and are left running
+    auto wait_tile = [&](bool fp4_ahead) {
+      if (fp4_ahead) __builtin_amdgcn_s_waitcnt(kWaitVm4);
+      else __builtin_amdgcn_s_waitcnt(0);
     };
 
     auto issue = [&](int t, uint8_t* buf) {
       const bool inA = t < ntA;
       if constexpr (FP4) {
-        if (inA && fp4a) {
-          const int r0 = t * TR;
-          const int64_t e0 = h * p.a.head_stride + int64_t(r0) * p.a.row_stride;
-          const int left = p.a.n - r0;
-          const uint32_t pbytes = left > 0 ? uint32_t(left) * (D / 2) : 0u;
-          const __amdgpu_buffer_rsrc_t rk = rsrc(p.a.k + e0 / 2, pbytes), rv = rsrc(p.a.v + e0 / 2, pbytes);
-          const __amdgpu_buffer_rsrc_t rks = rsrc(p.a.ks + e0 / 16, pbytes / 8);
-          const __amdgpu_buffer_rsrc_t rvs = rsrc(p.a.vs + e0 / 16, pbytes / 8);
-          const uint32_t off = uint32_t(fr) * (D / 2) + fq * 16;
-          kq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-          vq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-          const uint32_t soff = uint32_t(fr) * (D / 16) + fq * 2;
-          kqs = __builtin_amdgcn_raw_buffer_load_b16(rks, soff, 0, 0);
-          vqs = __builtin_amdgcn_raw_buffer_load_b16(rvs, soff, 0, 0);
-          return;
-        }
+        if (inA && fp4a) return;   // FP4 tiles come through registers, loaded ahead
       }
       const int r0 = (inA ? t : t - ntA) * TR;                  // first row of the tile in the segment
       const int64_t rp = (inA ? sa_rs : p.b.row_stride) * 2;     // row pitch in bytes
@@ -778,9 +791,20 @@ void attn_bf16_direct_kernel(Params p) {
       }
     };
 
-    issue(t0, smem + (t0 & 1) * DT_BUF);
-    if (fp4a && t0 < ntA) dequant_store(smem + (t0 & 1) * DT_BUF, DT_TILE, TR - 1);
-    __builtin_amdgcn_s_waitcnt(0);
+    if (FP4 && fp4_tile(t0)) {
+      load_fp4(t0, true);
+      load_fp4(t0, false);
+      dequant_half(smem + (t0 & 1) * DT_BUF, DT_TILE, TR - 1, true);
+      dequant_half(smem + (t0 & 1) * DT_BUF, DT_TILE, TR - 1, false);
+    } else {
+      issue(t0, smem + (t0 & 1) * DT_BUF);
+    }
+    const bool ahead0 = FP4 && t0 + 1 < t1 && fp4_tile(t0 + 1);
+    if (ahead0) {
+      load_fp4(t0 + 1, true);
+      load_fp4(t0 + 1, false);
+    }
+    wait_tile(ahead0);
     __syncthreads();
 
     for (int t = t0; t < t1; ++t) {
@@ -843,13 +867,17 @@ void attn_bf16_direct_kernel(Params p) {
       __builtin_amdgcn_s_setprio(0);
       softmax_update<D>(s, p.c, m_run, l_run, oacc, pb);
       if constexpr (FP4) {
-        // next tile's FP4 data -> bf16 at low priority, next to the softmax; when the next
-        // tile is not FP4 (or past the piece) the stores go to a 16 KB scratch area above the
-        // two buffers instead (K and V rows folded onto 64 rows), so no branch is needed
-        if (u2 == SUB - 1) {
-          const bool real = fp4a && t + 1 < t1 && t + 1 < ntA;
-          dequant_store(real ? smem + ((t + 1) & 1) * DT_BUF : smem + 2 * DT_BUF,
-                        real ? DT_TILE : 0, real ? TR - 1 : BN - 1);
+        // next tile's FP4 data (loaded a tile ahead) -> bf16 at low priority, next to the
+        // softmax: K in the first sub-tile, V in the last; the freed registers then take the
+        // loads of the tile after. When the next tile is not FP4 (or past the piece) the
+        // stores go to a 16 KB scratch area above the two buffers instead (K and V rows folded
+        // onto 64 rows), so no branch is needed
+        if (u2 == 0 || u2 == SUB - 1) {
+          const bool k_half = u2 == 0;
+          const bool real = t + 1 < t1 && fp4_tile(t + 1);
+          dequant_half(real ? smem + ((t + 1) & 1) * DT_BUF : smem + 2 * DT_BUF,
+                       real ? DT_TILE : 0, real ? TR - 1 : BN - 1, k_half);
+          if (t + 2 < t1 && fp4_tile(t + 2)) load_fp4(t + 2, k_half);
         }
       }
       __builtin_amdgcn_s_setprio(1);
@@ -882,7 +910,7 @@ void attn_bf16_direct_kernel(Params p) {
       __builtin_amdgcn_s_setprio(0);
       }
 
-      __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of tile t+1 have landed
+      wait_tile(FP4 && t + 2 < t1 && fp4_tile(t + 2));   // this wave's direct loads of tile t+1 have landed
       __syncthreads();
     }
 
