@@ -817,8 +817,8 @@ void attn_bf16_direct_kernel(Params p) {
       const bool inA = t < ntA;
       const int r0 = (inA ? t : t - ntA) * TR + u2 * BN;       // first row of the sub-tile
       const int seg_left = (inA ? na : nb) - r0;
-      // a sub-tile wholly past the end is skipped (FP4: computed fully masked instead, so the
-      // last sub-tile always reaches the dequantising store of the next tile)
+      // a sub-tile wholly past the end is skipped (FP4: computed fully masked instead, so every
+      // sub-tile reaches its share of the next tile's dequantisation and the loads after it)
       if (!FP4 && seg_left <= 0) continue;
       const int key0 = (inA ? 0 : na) + r0;
 
