@@ -167,11 +167,42 @@ def cpu_baseline(shape):
         m.commit(k.values, v.values)
     dt = time.perf_counter() - t0
     stream_time = dt * shape.heads / Hs
+    extra = {}
+    # the same stream over the oracle's FP4 store (codec included), for 1 of the 12 heads
+    sub1 = synth.shrink(shape, heads=1)
+    m4 = LayerModel(sub1.sink_frames, sub1.window_frames, sub1.chunk_frames,
+                    sub1.tokens_per_frame, 1, sub1.head_dim, kv_format="fp4")
+    inputs1 = [synth.chunk_inputs(sub1, 0, 0, c) for c in range(shape.chunks)]
+    t0 = time.perf_counter()
+    for q, k, v in inputs1:
+        m4.attn_chunk(q.values, k.values, v.values)
+        m4.commit(k.values, v.values, k.bits, v.bits)
+    dt4 = time.perf_counter() - t0
+    extra["fp4_stream"] = {"value": round(shape.n_query * shape.chunks / (dt4 * shape.heads), 3),
+                           "unit": "query-tokens/s",
+                           "sample": f"the {shape.chunks}-chunk stream over an FP4 store, 1/{shape.heads} heads, "
+                                     f"{dt4:.1f} s measured, scaled by heads"}
+    # one layer of the prompt-switch recache (12 held frames, 512 text tokens), 1 head
+    mr = LayerModel(sub1.sink_frames, sub1.window_frames, sub1.chunk_frames,
+                    sub1.tokens_per_frame, 1, sub1.head_dim)
+    for q, k, v in inputs1[:4]:
+        mr.commit(k.values, v.values)
+    rows = len(mr.held()) * sub1.tokens_per_frame
+    rin = synth.recache_inputs(sub1, 0, rows, 512)
+    t0 = time.perf_counter()
+    mr.recache(*(x.values for x in rin))
+    dtr = time.perf_counter() - t0
+    extra["recache_30_layers"] = {"value": round(rows / (dtr * shape.heads), 3),
+                                  "unit": "query-tokens/s",
+                                  "sample": f"one layer's recache ({rows} rows: block-causal self + 512-key "
+                                            f"cross), 1/{shape.heads} heads, {dtr:.1f} s measured, "
+                                            "scaled by heads (30 layers: the same rate)"}
     return {"value": round(shape.n_query * shape.chunks / stream_time, 3), "unit": "query-tokens/s",
             "cores": int(threads), "kind": "oracle",
             "sample": (f"fp64 oracle, the whole {shape.chunks}-chunk stream (attention + commit) "
                        f"for {Hs}/{shape.heads} heads x {shape.n_query} rows, {dt:.1f} s measured, "
-                       f"scaled by heads to {shape.heads}")}
+                       f"scaled by heads to {shape.heads}"),
+            "other_workloads": extra}
 
 
 def stack_row(torch, shape, Cache, attn_flops, kv_format, pool):
