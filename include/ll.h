@@ -130,9 +130,9 @@ ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const voi
  * ll_attn_chunk does, and
  *   ox = softmax(scale * qx K_text^T) V_text over all n_text text keys (no mask),
  * with qx, ox: [C*T, H, D] and k_text, v_text: [n_text, H, D], n_text >= 1, in the cache's
- * dtype (the text K/V are never quantised). For a bf16 head_dim-128 cache both parts run in
- * one kernel launch (the cross blocks take the compute units the self-attention leaves
- * idle); otherwise as two launches on `stream`. Errors as ll_attn_chunk, plus LL_EINVAL for a
+ * dtype (the text K/V are never quantised). For a dense bf16 head_dim-128 cache both parts
+ * run in one kernel launch (the cross blocks take the compute units the self-attention leaves
+ * idle); otherwise (FP4 store, head_dim 64, fp32) as two launches on `stream`. Errors as ll_attn_chunk, plus LL_EINVAL for a
  * NULL text pointer or an n_text out of range. */
 ll_status ll_attn_chunk_cross(ll_cache* cache, int32_t layer, const void* q, const void* k,
                               const void* v, const void* qx, const void* k_text,

@@ -445,8 +445,8 @@ def test_attn_chunk_cross_fused(heads, T, n_text):
 
 
 def test_attn_chunk_cross_other_shapes():
-    """head_dim 64 (bf16), fp32 and an FP4 cache: the same results through two launches
-    (head_dim 64, fp32) or the fused FP4 kernel."""
+    """head_dim 64 (bf16), fp32 and an FP4 cache: the same results when the self and cross
+    parts run as two launches (only a dense bf16 head_dim-128 cache fuses them)."""
     log("case: cross-attention, head_dim 64")
     _cross_stream(synth.shrink(synth.CONFIGS["layer"], name="cross-d64", heads=2, head_dim=64,
                                tokens_per_frame=72), 5, 50)
