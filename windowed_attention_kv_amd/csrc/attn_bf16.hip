@@ -35,6 +35,7 @@
 // through registers and stored transposed).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 
@@ -570,7 +571,11 @@ void attn_bf16_direct_kernel(Params p) {
   __shared__ int s_last;
 
   // XCD-aware order: workgroup ids are dealt round-robin over the 8 XCDs; each XCD gets a
-  // contiguous range of logical ids, so the query blocks of one head share an L2
+  // contiguous range of logical ids, so the query blocks of one head share an L2. Under the
+  // split schedule each XCD instead gets its proportional share of the main pieces (a
+  // contiguous range of blocks) and of the spare workgroups, whose block-major tail ranges
+  // then cover that XCD's own blocks: the tail tiles stay in the L2 that serves them, and no
+  // XCD carries more main pieces than in a whole-block launch.
   // (ids from n_self_wg on are the fused cross-attention workgroups: they keep their ids, so
   // they are dispatched after every self-attention workgroup)
   const int G = p.n_wg;
@@ -579,7 +584,15 @@ void attn_bf16_direct_kernel(Params p) {
   if (bid < p.n_self_wg) {
     const int xcd = bid & 7, idx = bid >> 3;
     const int qd = p.n_self_wg >> 3, rm = p.n_self_wg & 7;
-    g = (xcd < rm ? xcd * (qd + 1) : rm * (qd + 1) + (xcd - rm) * qd) + idx;
+    const int pre0 = xcd * qd + min(xcd, rm);   // ids dealt to the XCDs before this one
+    g = pre0 + idx;
+    if (p.split) {
+      const int nb = p.H * p.n_qblk;
+      const int pre1 = pre0 + qd + (xcd < rm ? 1 : 0);
+      const int m0 = int(int64_t(pre0) * nb / p.n_self_wg);
+      const int m1 = int(int64_t(pre1) * nb / p.n_self_wg);
+      g = idx < m1 - m0 ? m0 + idx : nb + (pre0 - m0) + (idx - (m1 - m0));
+    }
   }
 
   const int tid = threadIdx.x;
@@ -919,46 +932,69 @@ void attn_bf16_direct_kernel(Params p) {
       // The piece state is stored and read back with agent-scope (L2-coherent) accesses, and
       // the counter bump is preceded by one release fence (write-back of dirty L2 lines): no
       // acquire fence, whose L2 invalidation would evict the K/V every other workgroup on
-      // the XCD is reusing. The merging workgroup reads only after its counter bump returned
-      // the completing count.
-      float* sp = p.part + int64_t(slot) * SS::SLOT_FLOATS + wave * 64 + lane;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          __hip_atomic_store(sp + (db * 16 + i) * NW * 64, oacc[db][i], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sp + 64 * NW * 64, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sp + 65 * NW * 64, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are complete
-      __syncthreads();
+      // the XCD is reusing. The merging workgroup reads only after an atomic on the counter
+      // returned the completing count.
       const int64_t bu0 = int64_t(blk) * tail;                   // the block's first tail unit
       const int gs_first = int(range_of(bu0, UT, GS));
       const int gs_last = int(range_of(bu0 + tail - 1, UT, GS));
-      if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t old = __hip_atomic_fetch_add(p.cnt + blk, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        const int last = int(old) == gs_last - gs_first + 1;   // main piece + tail pieces - 1
-        if (last) __hip_atomic_store(p.cnt + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last;
+      const int n_tail_pieces = gs_last - gs_first + 1;
+      // The main piece first looks at the counter: when every tail piece has already arrived
+      // (the usual case when the spare workgroups have less work than a main piece), it
+      // merges the tails into its own registers and never publishes its state, which saves
+      // the write and read-back of one slot per block at the end of the launch.
+      bool from_regs = false;
+      if (!spare) {
+        if (tid == 0) {
+          const uint32_t c = __hip_atomic_load(p.cnt + blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int done = int(c) == n_tail_pieces;
+          if (done) __hip_atomic_store(p.cnt + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_last = done;
+        }
+        __syncthreads();
+        from_regs = s_last != 0;
+        __syncthreads();   // s_last is written again below
       }
-      __syncthreads();
-      if (!s_last) continue;
-      // merge: the main piece, then the tail pieces in range order (the result does not
-      // depend on which workgroup merges), online: the sum is rescaled whenever a piece brings
-      // a larger running max. Reads use buffer loads with the agent-scope (sc1) cache policy,
-      // the encoding of an agent-scope atomic load; as plain loads they may be issued back to
-      // back. A piece's 66 values are loaded into registers before any is used (scheduling
-      // barrier): left to itself, the compiler waited after every load in the FP4
-      // instantiation, whose registers run at the limit, and a merge of many pieces then took
-      // hundreds of microseconds.
-      const __amdgpu_buffer_rsrc_t rpart = rsrc(p.part, 0xFFFFFFFFu);
-      float m_all = kNoMax;
+      if (!from_regs) {
+        float* sp = p.part + int64_t(slot) * SS::SLOT_FLOATS + wave * 64 + lane;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16_t{};
-      l_run = 0.f;
-      for (int gs = gs_first - 1; gs <= gs_last; ++gs) {
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            __hip_atomic_store(sp + (db * 16 + i) * NW * 64, oacc[db][i], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sp + 64 * NW * 64, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sp + 65 * NW * 64, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are complete
+        __syncthreads();
+        if (tid == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          const uint32_t old = __hip_atomic_fetch_add(p.cnt + blk, 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+          const int last = int(old) == n_tail_pieces;   // main piece + tail pieces - 1
+          if (last) __hip_atomic_store(p.cnt + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_last = last;
+        }
+        __syncthreads();
+        if (!s_last) continue;
+      }
+      // merge: the main piece, then the tail pieces in range order (the result does not
+      // depend on which workgroup merges: starting from the main piece's registers is the
+      // same arithmetic as loading it first into a zero state), online: the sum is rescaled
+      // whenever a piece brings a larger running max. Reads use buffer loads with the
+      // agent-scope (sc1) cache policy, the encoding of an agent-scope atomic load; as plain
+      // loads they may be issued back to back. A piece's 66 values are loaded into registers
+      // before any is used (scheduling barrier): left to itself, the compiler waited after
+      // every load in the FP4 instantiation, whose registers run at the limit, and a merge of
+      // many pieces then took hundreds of microseconds.
+      const __amdgpu_buffer_rsrc_t rpart = rsrc(p.part, 0xFFFFFFFFu);
+      float m_all = m_run;
+      if (!from_regs) {
+        m_all = kNoMax;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16_t{};
+        l_run = 0.f;
+      }
+      for (int gs = from_regs ? gs_first : gs_first - 1; gs <= gs_last; ++gs) {
         const int sl = gs < gs_first ? blk : nblk + gs + blk;
         const uint32_t base = uint32_t((int64_t(sl) * SS::SLOT_FLOATS + wave * 64 + lane) * 4);
         float b[SS::REGS];
@@ -1005,19 +1041,34 @@ void attn_bf16_direct_kernel(Params p) {
   }
 }
 
+// One flag per device and kernel: the dynamic-LDS limit is a per-device attribute of the
+// kernel, so it is raised once on every device the kernel is launched on.
+struct DeviceFlags {
+  static constexpr int kMax = 64;
+  std::atomic<bool> set[kMax] = {};
+};
+
+int allow_lds(const void* kern, int bytes, DeviceFlags& flags, char* err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    snprintf(err, 256, "no current device");
+    return 1;
+  }
+  if (dev < DeviceFlags::kMax && flags.set[dev].load(std::memory_order_acquire)) return 0;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) {
+    snprintf(err, 256, "cannot set %d bytes of LDS", bytes);
+    return 1;
+  }
+  if (dev < DeviceFlags::kMax) flags.set[dev].store(true, std::memory_order_release);
+  return 0;
+}
+
 template <int NW, int SUB, bool FP4, bool CROSS>
 int launch_direct(const Params& p, int grid, hipStream_t stream, char* err) {
   auto kern = attn_bf16_direct_kernel<NW, SUB, FP4, CROSS>;
   constexpr int DT_LDS = DtCfg<SUB>::LDS + (FP4 ? BN * DT_ROW : 0);
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, DT_LDS) != hipSuccess) {
-      snprintf(err, 256, "cannot set %d bytes of LDS", DT_LDS);
-      return 1;
-    }
-    attr_set = true;
-  }
+  static DeviceFlags attr_set;
+  if (int r = allow_lds(reinterpret_cast<const void*>(kern), DT_LDS, attr_set, err)) return r;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), DT_LDS, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -1031,15 +1082,8 @@ template <int D, int NW, bool FP4>
 int launch_t(const Params& p, int grid, hipStream_t stream, char* err) {
   using C = Cfg<D, NW>;
   auto kern = attn_bf16_kernel<D, NW, FP4>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess) {
-      snprintf(err, 256, "cannot set %d bytes of LDS", C::LDS);
-      return 1;
-    }
-    attr_set = true;
-  }
+  static DeviceFlags attr_set;
+  if (int r = allow_lds(reinterpret_cast<const void*>(kern), C::LDS, attr_set, err)) return r;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -1126,11 +1170,15 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
       return launch_attention_bf16(cx, stream, err);
     }
     if (a.vis.mode == 0 && a.ws && a.n_cu > blocks && blocks <= a.ws_blocks) {
-      // Split when the best main/tail cut is clearly shorter than one whole block. Cost in
-      // key tiles, with kPieceCost tiles per piece for its prologue (Q load, first tile not
+      // Split when the best main/tail cut is shorter than one whole block. Cost in key
+      // tiles, with kPieceCost tiles per piece for its prologue (Q load, first tile not
       // overlapped) and its publish (a spare workgroup runs at most ceil(span/tail) + 1
-      // pieces), and kMergeCost per piece the merging workgroup reads. Measured on MI355X:
-      // 12 heads x 4680 rows (228 blocks) is faster whole, 1-6 heads are faster split.
+      // pieces), and kMergeCost per piece the merging workgroup reads. The model's best cut
+      // matches the measured best on MI355X at 1 to 12 heads x 4680 rows (at 12 heads, 228
+      // blocks: main 168 of 184 tiles, 3% faster than whole blocks; it predicts 5%, since
+      // the 28 extra busy CUs lower the sustained clock). The decision ignores fused
+      // cross-attention blocks, so the self part of a fused launch runs the same schedule
+      // (and gives the same bits) as a plain chunk call.
       constexpr int64_t kPieceCost = 4, kMergeCost = 1;
       const int nt = (p.a.n + TR - 1) / TR + (p.b.n + TR - 1) / TR;
       const int64_t spare = a.n_cu - blocks;
@@ -1153,7 +1201,7 @@ int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
       }
       const int64_t ut = int64_t(blocks) * (nt - best_main);
       const int64_t gs = ut < spare ? ut : spare;
-      if (best_main < nt && best * 100 < int64_t(nt) * 85 && 2 * (blocks + gs) <= a.ws_slots) {
+      if (best_main < nt && best * 100 < int64_t(nt) * 97 && 2 * (blocks + gs) <= a.ws_slots) {
         uint8_t* ws = static_cast<uint8_t*>(a.ws);
         p.split = 1;
         p.nt = nt;
