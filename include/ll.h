@@ -148,6 +148,18 @@ ll_status ll_attn_chunk_cross(ll_cache* cache, int32_t layer, const void* q, con
 ll_status ll_cache_commit(ll_cache* cache, int32_t layer, const void* k, const void* v,
                           void* stream);
 
+/* ll_cache_commit for the layers first_layer .. first_layer + n_layers - 1 in one launch
+ * (one launch per 32 layers): layer first_layer + i takes k[i], v[i] ([C*T, H, D] device
+ * pointers; k and v are HOST arrays of n_layers pointers, read during the call only). Each
+ * layer gets exactly what ll_cache_commit would give it (its own frame count and shot), so
+ * layers may be at different frames. Committing every layer of a denoise step at once moves
+ * enough bytes per launch to run the commit at full HBM bandwidth ("为什么视频生成是一个基础设施
+ * 问题", §3 and §4: KV-cache update and movement become visible costs once the denoise steps
+ * are few). Every layer is validated before anything is enqueued; on any error no layer's
+ * metadata changes. LL_EINVAL for a bad handle, layer range, or a NULL / misaligned pointer. */
+ll_status ll_cache_commit_layers(ll_cache* cache, int32_t first_layer, int32_t n_layers,
+                                 const void* const* k, const void* const* v, void* stream);
+
 /* Prompt-switch recache of `layer` ("LongLive" page, 方法 §1 KV 重缓存). The rows are the
  * frames the layer holds, in ascending frame id (n = held_frames * T rows):
  *   q, k, v, qx, o, ox: [n, H, D]; k_text, v_text: [n_text, H, D], n_text >= 1.

@@ -383,3 +383,98 @@ def test_kv_quant_validation(fake):
     fake.llfake_reset()
     assert fake.ll_kv_quant(P, 3, 32, P, P, None) == 0
     assert _records(fake)[0][0] == 2
+
+
+def _ptr_array(vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+@pytest.mark.parametrize("kv_format", ["dense", "fp4"])
+def test_commit_layers_matches_per_layer_commits(fake, kv_format):
+    """ll_cache_commit_layers gives every layer exactly the plan ll_cache_commit would:
+    layers at different frame counts and shots (a new shot on layer 2 only), replayed on slot
+    lists like the single-layer scatter, with each layer's own source and destination
+    pointers; the state of every committed layer advances by one chunk."""
+    S, W, C, T, L = 3, 9, 3, 16, 4
+    dtype = "bf16"
+    h, _ = _create(fake, layers=L, sink_frames=S, window_frames=W, chunk_frames=C, dtype=dtype,
+                   kv_format=kv_format)
+    # layer 0 runs two chunks ahead, layer 2 starts a new shot after its third chunk
+    for _ in range(2):
+        assert fake.ll_cache_commit(h, 0, P, P, None) == 0
+    sims = [[-1] * (S + W) for _ in range(L)]
+    sims[0] = ring.slot_map(2 * C, S, W)
+    frames = [2 * C if l == 0 else 0 for l in range(L)]
+    shots = [0] * L
+    for chunk in range(8):
+        if chunk == 3:
+            assert fake.ll_cache_new_shot(h, 2) == 0
+            shots[2] = frames[2]
+        ks = [(1 << 24) + 4096 * (i + 1) for i in range(3)]
+        vs = [(1 << 25) + 4096 * (i + 1) for i in range(3)]
+        fake.llfake_reset()
+        assert fake.ll_cache_commit_layers(h, 1 - (chunk % 2), 3, _ptr_array(ks), _ptr_array(vs), None) == 0
+        recs = _records(fake)
+        first = 1 - (chunk % 2)
+        assert [k for k, _ in recs] == [5, 5, 5]
+        for i, (_, rec) in enumerate(recs):
+            layer = first + i
+            F, B = frames[layer], shots[layer]
+            assert rec[8] == 3 and rec[9] == i and rec[10] == F
+            assert (rec[14], rec[15]) == (ks[i], vs[i])
+            # replay: frame F+r enters window slot (F+r) mod W after moving a leaving sink frame
+            lo, hi, sp0 = rec[11], rec[12], rec[13]
+            for r in range(C):
+                dst = (F + r) % W
+                if lo <= r < hi:
+                    sims[layer][sp0 + (r - lo)] = sims[layer][dst]
+                sims[layer][dst] = F + r
+            frames[layer] = F + C
+            want = ring.slot_map(frames[layer], S, W, shots[layer])
+            assert [x if want[j] >= 0 else -1 for j, x in enumerate(sims[layer])] == want
+            assert _state(fake, h, layer, S + W) == (frames[layer], want)
+        # destination planes: one layer apart, K then V; FP4 also passes its scale planes
+        dk = [rec[16] for _, rec in recs]
+        assert dk[1] - dk[0] == dk[2] - dk[1] > 0
+        assert all(rec[17] > rec[16] for _, rec in recs)
+        if kv_format == "fp4":
+            assert all(rec[18] > rec[16] and rec[19] > rec[17] for _, rec in recs)
+        else:
+            assert all(rec[18] == 0 and rec[19] == 0 for _, rec in recs)
+    assert _state(fake, h, 3, S + W)[0] == frames[3]
+    fake.ll_cache_destroy(h)
+
+
+def test_commit_layers_errors_change_nothing(fake):
+    """Bad layer ranges, NULL pointer arrays, a misaligned or NULL pointer for one layer, and
+    a launch failure: LL_EINVAL / LL_EDEVICE, nothing enqueued (except the failing launch), no
+    layer's frame count changed."""
+    S, W, C, L = 3, 9, 3, 4
+    h, _ = _create(fake, layers=L, sink_frames=S, window_frames=W, chunk_frames=C, dtype="bf16")
+    good = [1 << 24] * L
+    bad_align = list(good)
+    bad_align[2] = (1 << 24) + 8
+    with_null = list(good)
+    with_null[1] = 0
+    cases = [
+        (0, 0, good, good, _lib.LL_EINVAL),
+        (-1, 2, good, good, _lib.LL_EINVAL),
+        (2, 3, good, good, _lib.LL_EINVAL),
+        (0, 5, good + [1 << 24], good + [1 << 24], _lib.LL_EINVAL),
+        (0, 4, bad_align, good, _lib.LL_EINVAL),
+        (0, 4, good, with_null, _lib.LL_EINVAL),
+    ]
+    for first, n, ks, vs, want in cases:
+        fake.llfake_reset()
+        assert fake.ll_cache_commit_layers(h, first, n, _ptr_array(ks), _ptr_array(vs), None) == want
+        assert fake.llfake_count() == 0
+        assert all(_state(fake, h, l, S + W)[0] == 0 for l in range(L))
+    assert fake.ll_cache_commit_layers(h, 0, 2, None, _ptr_array(good), None) == _lib.LL_EINVAL
+    assert fake.ll_cache_commit_layers(None, 0, 2, _ptr_array(good), _ptr_array(good), None) == _lib.LL_EINVAL
+    fake.llfake_reset()
+    fake.llfake_fail_next(1)
+    assert fake.ll_cache_commit_layers(h, 0, 4, _ptr_array(good), _ptr_array(good), None) == _lib.LL_EDEVICE
+    assert all(_state(fake, h, l, S + W)[0] == 0 for l in range(L))
+    assert fake.ll_cache_commit_layers(h, 0, 4, _ptr_array(good), _ptr_array(good), None) == 0
+    assert all(_state(fake, h, l, S + W)[0] == C for l in range(L))
+    fake.ll_cache_destroy(h)

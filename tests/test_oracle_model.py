@@ -278,3 +278,50 @@ def test_rising_score_inputs_move_the_running_max(D):
             steps += before.size
             jumps += int(np.sum(after > before + 8))
     assert jumps > 0.01 * steps, (jumps, steps)
+
+
+def test_export_fp4_is_the_committed_frames_encoded_in_slot_order():
+    """Pin of LayerModel.export_fp4, the reference of every FP4 export comparison. After every
+    commit of a multi-shot stream, and after a recache, its planes equal an assembly built
+    without the model: each held frame's slot from the frame-by-frame slot simulation of
+    test_oracle_ring (explicit window FIFO and sink slots, not ring.slot_map), its codes and
+    scales from fp4.quantize of the bf16 bits this test committed for that frame, every other
+    row marked empty."""
+    from test_oracle_ring import slot_simulation
+    shape = synth.shrink(SMALL_LAYER, tokens_per_frame=8, window_frames=4)
+    S, W, C, T, H, D = (shape.sink_frames, shape.window_frames, shape.chunk_frames,
+                        shape.tokens_per_frame, shape.heads, shape.head_dim)
+    shots, n_chunks = (5,), 10
+    snaps = {F: slots for F, B, slots, held in
+             slot_simulation(n_chunks * C, C, S, W, shot_starts={c * C for c in shots})}
+    m = _model(shape, kv_format="fp4")
+    bits = {}                # frame -> (K bits [T, H, D], V bits)
+
+    def check():
+        slots = snaps[m.F]
+        kp, ks, vp, vs, valid = m.export_fp4()
+        rows = T * H
+        for slot, f in enumerate(slots):
+            sl = slice(slot * rows, (slot + 1) * rows)
+            assert bool(valid[sl].all()) == (f >= 0) and bool(valid[sl].any()) == (f >= 0)
+            if f < 0:
+                continue
+            for got_p, got_s, b in ((kp, ks, bits[f][0]), (vp, vs, bits[f][1])):
+                wp, ws = fp4.quantize(b.reshape(rows, D))
+                assert np.array_equal(got_p[sl], wp) and np.array_equal(got_s[sl], ws), (m.F, slot, f)
+
+    for c in range(n_chunks):
+        _, k, v = synth.chunk_inputs(shape, 0, 0, c)
+        m.commit(k.values, v.values, k.bits, v.bits)
+        for i in range(C):
+            bits[c * C + i] = (k.bits[i * T:(i + 1) * T], v.bits[i * T:(i + 1) * T])
+        if c + 1 in shots:       # the simulation opens a shot at the boundary frame itself
+            m.new_shot()
+        check()
+    held = m.held()
+    ins = synth.recache_inputs(shape, 0, len(held) * T, 8)
+    q, k, v, qx, kt, vt = ins
+    m.recache(q.values, k.values, v.values, qx.values, kt.values, vt.values, k.bits, v.bits)
+    for r, f in enumerate(held):
+        bits[f] = (k.bits[r * T:(r + 1) * T], v.bits[r * T:(r + 1) * T])
+    check()

@@ -119,6 +119,17 @@ class Cache:
         check(self._lib, self._lib.ll_cache_commit(self.handle, layer, self._check(k, n, "k"),
                                                    self._check(v, n, "v"), _stream(self.device)))
 
+    def commit_layers(self, first_layer, ks, vs):
+        """Commit one chunk's K/V into layers first_layer .. first_layer + len(ks) - 1 with
+        one launch (ks[i], vs[i] go to layer first_layer + i)."""
+        n = self.n_chunk
+        if len(ks) != len(vs) or not ks:
+            raise ValueError("commit_layers: ks and vs must be non-empty and of equal length")
+        kp = (ctypes.c_void_p * len(ks))(*[self._check(t, n, "k").value for t in ks])
+        vp = (ctypes.c_void_p * len(vs))(*[self._check(t, n, "v").value for t in vs])
+        check(self._lib, self._lib.ll_cache_commit_layers(self.handle, first_layer, len(ks), kp, vp,
+                                                          _stream(self.device)))
+
     def new_shot(self, layer=None):
         """Shot boundary (multi-shot sink): the next committed frame of `layer` (default:
         every layer) starts a new shot whose first S frames become the sink."""

@@ -193,6 +193,119 @@ __global__ __launch_bounds__(256) void scatter_fp4_kernel(ScatterP p, int32_t n_
   }
 }
 
+// ---- batched commit: one chunk into many layers per launch ----
+// A single layer's commit moves ~57 MB (dense) or ~37 MB (FP4) at the layer shape, too little
+// for one launch to ramp up to full HBM bandwidth; committing every layer of a denoise step
+// in one launch moves 30x that. blockIdx.y = 2 * layer + (K | V); the per-layer pointers and
+// ring position travel in the kernel arguments.
+struct LayerP {
+  const uint8_t* src[2];
+  uint8_t* dst[2];
+  uint8_t* dst_scales[2];
+  int32_t ring0;                       // window slot of the chunk's first frame
+  int32_t spill_lo, spill_hi, spill_slot0;
+};
+
+struct CommitLayersP {
+  int32_t H, D, T, W, slots, es;
+  int32_t n_rows;                      // token rows of the chunk (C * T)
+  int32_t units;                       // dense: 16-byte units per token row; fp4: 64-element groups
+  LayerP l[kMaxCommitLayers];
+};
+
+constexpr int kCommitRows = 4;         // dense: token rows per workgroup
+
+// window slot of frame rank r of the chunk (ring0 < W, r < C <= W)
+__device__ __forceinline__ int32_t commit_slot(int32_t ring0, int32_t r, int32_t W) {
+  const int32_t k = ring0 + r;
+  return k >= W ? k - W : k;
+}
+
+// dense: each thread takes the same 16-byte unit of each of the workgroup's kCommitRows token
+// rows, issuing all of its loads before its stores
+__global__ __launch_bounds__(256) void commit_layers_dense_kernel(CommitLayersP p, int32_t uph_log2) {
+  const int which = blockIdx.y & 1;
+  const int layer = blockIdx.y >> 1;
+  const uint8_t* const src = p.l[layer].src[which];
+  uint8_t* const dst = p.l[layer].dst[which];
+  const int32_t ring0 = p.l[layer].ring0;
+  const int32_t lo = p.l[layer].spill_lo, hi = p.l[layer].spill_hi, s0 = p.l[layer].spill_slot0;
+  const int32_t row_bytes = p.D * p.es;
+  const int32_t uph = row_bytes >> 4;
+  const int64_t head_plane = int64_t(p.slots) * p.T * row_bytes;
+  const int32_t tr0 = blockIdx.x * kCommitRows;
+  int64_t drow[kCommitRows], srow[kCommitRows];
+  bool live[kCommitRows];
+#pragma unroll
+  for (int i = 0; i < kCommitRows; ++i) {
+    const int32_t tr = tr0 + i;
+    live[i] = tr < p.n_rows;
+    const int32_t r = tr / p.T, t = tr - r * p.T;
+    drow[i] = (int64_t(commit_slot(ring0, r, p.W)) * p.T + t) * row_bytes;
+    srow[i] = (r >= lo && r < hi) ? (int64_t(s0 + (r - lo)) * p.T + t) * row_bytes : -1;
+  }
+  for (int32_t u = threadIdx.x; u < p.units; u += blockDim.x) {
+    const int32_t h = u >> uph_log2, cc = u & (uph - 1);
+    const int64_t col = h * head_plane + cc * 16;
+    uint4 x[kCommitRows];
+#pragma unroll
+    for (int i = 0; i < kCommitRows; ++i)
+      if (live[i]) x[i] = *reinterpret_cast<const uint4*>(src + (int64_t(tr0 + i) * p.units + u) * 16);
+#pragma unroll
+    for (int i = 0; i < kCommitRows; ++i) {
+      if (!live[i]) continue;
+      uint4* dp = reinterpret_cast<uint4*>(dst + col + drow[i]);
+      if (srow[i] >= 0) {
+        // a sink frame leaves the window: its old 16 bytes move to the sink slot first (the
+        // same thread reads them, stores them there, then overwrites them)
+        const uint4 old = *dp;
+        *reinterpret_cast<uint4*>(dst + col + srow[i]) = old;
+      }
+      *dp = x[i];
+    }
+  }
+}
+
+// fp4: one thread per 64 elements (32 code bytes + one 4-byte scale word) of a (token, head)
+// row, kFp4Rows token rows per workgroup; a thread that overwrites a leaving sink frame's
+// codes first moves them (and their scales) to the sink slot
+__global__ __launch_bounds__(256) void commit_layers_fp4_kernel(CommitLayersP p, int32_t gph_log2) {
+  const int which = blockIdx.y & 1;
+  const int layer = blockIdx.y >> 1;
+  const uint8_t* const src = p.l[layer].src[which];
+  uint8_t* const dst = p.l[layer].dst[which];
+  uint8_t* const dsc = p.l[layer].dst_scales[which];
+  const int32_t ring0 = p.l[layer].ring0;
+  const int32_t lo = p.l[layer].spill_lo, hi = p.l[layer].spill_hi, s0 = p.l[layer].spill_slot0;
+  const int64_t head_rows = int64_t(p.slots) * p.T;
+  const int32_t tr0 = blockIdx.x * kFp4Rows;
+  const int32_t nr = min(kFp4Rows, p.n_rows - tr0);
+  for (int32_t i = threadIdx.x; i < nr * p.units; i += blockDim.x) {
+    const int32_t rl = i / p.units, g = i - rl * p.units;
+    const int32_t tr = tr0 + rl;
+    const int32_t r = tr / p.T, t = tr - r * p.T;
+    const int32_t h = g >> gph_log2, cc = g & ((1 << gph_log2) - 1);
+    uint4 pk0, pk1;
+    uint32_t sc;
+    quant64(src + (int64_t(tr) * p.units + g) * 128, pk0, pk1, sc);
+    const int64_t row = h * head_rows + int64_t(commit_slot(ring0, r, p.W)) * p.T + t;
+    uint4* dp = reinterpret_cast<uint4*>(dst + row * (p.D / 2) + cc * 32);
+    uint32_t* sp = reinterpret_cast<uint32_t*>(dsc + row * (p.D / 16) + cc * 4);
+    if (r >= lo && r < hi) {
+      const int64_t srow = h * head_rows + int64_t(s0 + (r - lo)) * p.T + t;
+      const uint4 o0 = dp[0], o1 = dp[1];
+      const uint32_t os = *sp;
+      uint4* sdp = reinterpret_cast<uint4*>(dst + srow * (p.D / 2) + cc * 32);
+      sdp[0] = o0;
+      sdp[1] = o1;
+      *reinterpret_cast<uint32_t*>(dsc + srow * (p.D / 16) + cc * 4) = os;
+    }
+    dp[0] = pk0;
+    dp[1] = pk1;
+    *sp = sc;
+  }
+}
+
 // standalone codec: one thread per 64 elements when the row length allows, else per 16
 __global__ __launch_bounds__(256) void quant64_kernel(const uint8_t* x, int64_t ngrp, uint8_t* packed,
                                                       uint8_t* scales) {
@@ -322,6 +435,57 @@ int launch_scatter(const ScatterArgs& a, void* stream, char* err) {
       const int blocks = n_units / units;
       hipLaunchKernelGGL(scatter_dense_kernel, dim3(blocks, 2), dim3(block_for(units)), 0, s, p, n_units, units,
                          1.0f / float(units), inv_t, uph == 8 ? 3 : (uph == 16 ? 4 : 5));
+    }
+  }
+  return finish(err);
+}
+
+int launch_commit_layers(const CommitLayersArgs& a, void* stream, char* err) {
+  if (a.n_layers <= 0) return 0;
+  if (a.fp4 && a.D % 64) {
+    snprintf(err, 256, "the FP4 store needs head_dim %% 64 == 0");
+    return 1;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t es = a.dtype == 1 ? 2 : 4;
+  const int32_t n_rows = a.C * a.T;
+  for (int32_t l0 = 0; l0 < a.n_layers; l0 += kMaxCommitLayers) {
+    const int32_t nl = min(kMaxCommitLayers, a.n_layers - l0);
+    CommitLayersP p{};
+    p.H = a.H;
+    p.D = a.D;
+    p.T = a.T;
+    p.W = a.W;
+    p.slots = a.slots;
+    p.es = es;
+    p.n_rows = n_rows;
+    for (int32_t i = 0; i < nl; ++i) {
+      const CommitLayer& c = a.layers[l0 + i];
+      LayerP& L = p.l[i];
+      L.src[0] = static_cast<const uint8_t*>(c.k_src);
+      L.src[1] = static_cast<const uint8_t*>(c.v_src);
+      L.dst[0] = static_cast<uint8_t*>(c.k_dst);
+      L.dst[1] = static_cast<uint8_t*>(c.v_dst);
+      L.dst_scales[0] = c.k_dst_scales;
+      L.dst_scales[1] = c.v_dst_scales;
+      L.ring0 = int32_t(c.first_ring % a.W);
+      L.spill_lo = c.spill_lo;
+      L.spill_hi = c.spill_hi;
+      L.spill_slot0 = c.spill_slot0;
+    }
+    if (a.fp4) {
+      const int32_t gph = a.D / 64;
+      p.units = a.H * gph;
+      const int blocks = (n_rows + kFp4Rows - 1) / kFp4Rows;
+      const int threads = min(256, (kFp4Rows * p.units + 63) / 64 * 64);
+      hipLaunchKernelGGL(commit_layers_fp4_kernel, dim3(blocks, 2 * nl), dim3(threads), 0, s, p,
+                         gph == 2 ? 1 : 0);
+    } else {
+      const int32_t uph = a.D * es / 16;             // 8, 16 or 32
+      p.units = a.H * uph;
+      const int blocks = (n_rows + kCommitRows - 1) / kCommitRows;
+      hipLaunchKernelGGL(commit_layers_dense_kernel, dim3(blocks, 2 * nl), dim3(block_for(p.units)), 0, s,
+                         p, uph == 8 ? 3 : (uph == 16 ? 4 : 5));
     }
   }
   return finish(err);

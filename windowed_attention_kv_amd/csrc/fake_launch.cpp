@@ -11,7 +11,7 @@
 namespace {
 
 struct Record {
-  int kind;              // 0 attention, 1 scatter, 2 quant, 3 export, 4 zero
+  int kind;              // 0 attention, 1 scatter, 2 quant, 3 export, 4 zero, 5 commit layer
   int64_t f[24];
 };
 
@@ -47,6 +47,22 @@ int launch_scatter(const ScatterArgs& a, void*, char* err) {
   Record r{1, {a.dtype, a.fp4, a.H, a.D, a.T, a.n_frames, a.n_lead, a.lead_slot0, a.ring_base, a.W,
                a.first_ring, a.slots, a.spill_lo, a.spill_hi, a.spill_slot0, 0}};
   g_log.push_back(r);
+  return 0;
+}
+
+// one record per layer of a batched commit
+int launch_commit_layers(const CommitLayersArgs& a, void*, char* err) {
+  if (maybe_fail(err)) return 1;
+  for (int i = 0; i < a.n_layers; ++i) {
+    const CommitLayer& c = a.layers[i];
+    Record r{5, {a.dtype, a.fp4, a.H, a.D, a.T, a.C, a.W, a.slots, a.n_layers, i, c.first_ring,
+                 c.spill_lo, c.spill_hi, c.spill_slot0,
+                 int64_t(reinterpret_cast<uintptr_t>(c.k_src)), int64_t(reinterpret_cast<uintptr_t>(c.v_src)),
+                 int64_t(reinterpret_cast<uintptr_t>(c.k_dst)), int64_t(reinterpret_cast<uintptr_t>(c.v_dst)),
+                 int64_t(reinterpret_cast<uintptr_t>(c.k_dst_scales)),
+                 int64_t(reinterpret_cast<uintptr_t>(c.v_dst_scales))}};
+    g_log.push_back(r);
+  }
   return 0;
 }
 

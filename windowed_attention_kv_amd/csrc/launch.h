@@ -90,6 +90,31 @@ struct ScatterArgs {
   int32_t slots = 0;
 };
 
+// One layer of a batched commit: the chunk's K/V (token-major, C frames) go to window slots
+// (first_ring + r) mod W, r = 0..C-1; for r in [spill_lo, spill_hi) the destination slot's
+// old contents first move to slot spill_slot0 + (r - spill_lo) (a sink frame leaving the
+// window), as in ScatterArgs.
+struct CommitLayer {
+  const void* k_src = nullptr;
+  const void* v_src = nullptr;
+  void* k_dst = nullptr;             // head-major planes [H][slots*T][D] (dense) or packed (fp4)
+  void* v_dst = nullptr;
+  uint8_t* k_dst_scales = nullptr;   // fp4 only
+  uint8_t* v_dst_scales = nullptr;
+  int64_t first_ring = 0;            // frame id of the chunk's first frame
+  int32_t spill_lo = 0, spill_hi = 0, spill_slot0 = 0;
+};
+
+// Commit of one chunk into n_layers layers of the same geometry in one launch per
+// kMaxCommitLayers layers (the per-layer table travels in the kernel arguments).
+constexpr int kMaxCommitLayers = 32;
+struct CommitLayersArgs {
+  int32_t dtype = 0, fp4 = 0;
+  int32_t H = 0, D = 0, T = 0, C = 0, W = 0, slots = 0;
+  int32_t n_layers = 0;
+  const CommitLayer* layers = nullptr;   // host array of n_layers entries
+};
+
 struct QuantArgs {
   const void* x = nullptr;
   int64_t rows = 0;
@@ -116,6 +141,7 @@ struct ExportArgs {
 // (at least 256 bytes).
 int launch_attention(const AttnArgs& a, void* stream, char* err);
 int launch_scatter(const ScatterArgs& a, void* stream, char* err);
+int launch_commit_layers(const CommitLayersArgs& a, void* stream, char* err);
 int launch_quant(const QuantArgs& a, void* stream, char* err);
 int launch_export(const ExportArgs& a, void* stream, char* err);
 // zero `bytes` (a multiple of 4) at p with a kernel on the stream

@@ -235,6 +235,45 @@ ll::ScatterArgs scatter_base(const ll_cache* c, int32_t layer) {
   return a;
 }
 
+// Validation shared by the single-layer and batched commits.
+ll_status check_commit(const ll_cache* cache, int32_t layer, const void* k, const void* v) {
+  if (ll_status s = check_layer(cache, layer)) return s;
+  if (ll_status s = check_ptr(k, "k")) return s;
+  if (ll_status s = check_ptr(v, "v")) return s;
+  const int64_t F = cache->frames[layer];
+  if (F + cache->d.chunk_frames >= (int64_t(1) << 31) - 1)
+    return fail(LL_ESTATE, "layer %d has committed %lld frames: frame ids must fit 31 bits", layer,
+                (long long)F);
+  return LL_OK;
+}
+
+// Where the next chunk of `layer` goes: frame F+r (r < C) enters window slot (F+r) mod W and
+// evicts frame e = F+r-W (C <= W, so e < F); a sink frame of the current shot (B <= e < B+S)
+// moves to sink slot W + (e - B) first.
+ll::CommitLayer commit_plan(const ll_cache* c, int32_t layer, const void* k, const void* v) {
+  const ll_cache_desc& d = c->d;
+  const int64_t F = c->frames[layer];
+  const int64_t S = d.sink_frames, C = d.chunk_frames, W = d.window_frames, B = c->shot[layer];
+  ll::CommitLayer p;
+  p.k_src = k;
+  p.v_src = v;
+  p.k_dst = plane(c, layer, c->L.k_off);
+  p.v_dst = plane(c, layer, c->L.v_off);
+  if (d.kv_format == LL_KV_FP4) {
+    p.k_dst_scales = plane(c, layer, c->L.ks_off);
+    p.v_dst_scales = plane(c, layer, c->L.vs_off);
+  }
+  p.first_ring = F;
+  const int64_t lo = std::max<int64_t>(0, B + W - F);
+  const int64_t hi = std::min<int64_t>(C, B + S + W - F);
+  if (lo < hi) {
+    p.spill_lo = int32_t(lo);
+    p.spill_hi = int32_t(hi);
+    p.spill_slot0 = int32_t(W + (F + lo - W - B));
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -371,35 +410,57 @@ ll_status ll_attn_chunk_cross(ll_cache* cache, int32_t layer, const void* q, con
 
 ll_status ll_cache_commit(ll_cache* cache, int32_t layer, const void* k, const void* v,
                           void* stream) {
-  if (ll_status s = check_layer(cache, layer)) return s;
-  if (ll_status s = check_ptr(k, "k")) return s;
-  if (ll_status s = check_ptr(v, "v")) return s;
-  const ll_cache_desc& d = cache->d;
-  const int64_t F = cache->frames[layer];
-  const int64_t S = d.sink_frames, C = d.chunk_frames;
-  if (F + C >= (int64_t(1) << 31) - 1)
-    return fail(LL_ESTATE, "layer %d has committed %lld frames: frame ids must fit 31 bits", layer,
-                (long long)F);
-  const int64_t W = d.window_frames, B = cache->shot[layer];
+  if (ll_status s = check_commit(cache, layer, k, v)) return s;
+  const ll::CommitLayer c = commit_plan(cache, layer, k, v);
   ll::ScatterArgs a = scatter_base(cache, layer);
-  a.n_frames = d.chunk_frames;
+  a.n_frames = cache->d.chunk_frames;
   a.n_lead = 0;
-  a.first_ring = F;
-  // frame F+r evicts frame e = F+r-W from its window slot (C <= W, so e < F); a sink frame
-  // of the current shot (B <= e < B+S) moves to sink slot W + (e - B)
-  const int64_t lo = std::max<int64_t>(0, B + W - F);
-  const int64_t hi = std::min<int64_t>(C, B + S + W - F);
-  if (lo < hi) {
-    a.spill_lo = int32_t(lo);
-    a.spill_hi = int32_t(hi);
-    a.spill_slot0 = int32_t(W + (F + lo - W - B));
-  }
+  a.first_ring = c.first_ring;
+  a.spill_lo = c.spill_lo;
+  a.spill_hi = c.spill_hi;
+  a.spill_slot0 = c.spill_slot0;
   a.k_src = k;
   a.v_src = v;
   char msg[256] = "";
   if (ll_status s = device_status(ll::launch_scatter(a, stream, msg), "commit launch", msg))
     return s;
-  cache->frames[layer] = F + C;
+  cache->frames[layer] += cache->d.chunk_frames;
+  return ok();
+}
+
+ll_status ll_cache_commit_layers(ll_cache* cache, int32_t first_layer, int32_t n_layers,
+                                 const void* const* k, const void* const* v, void* stream) {
+  if (!cache) return fail(LL_EINVAL, "cache handle is NULL");
+  if (!k || !v) return fail(LL_EINVAL, "k/v pointer array is NULL");
+  if (n_layers < 1 || first_layer < 0 || first_layer >= cache->d.num_layers ||
+      n_layers > cache->d.num_layers - first_layer)
+    return fail(LL_EINVAL, "layers [%d, %d + %d) out of range [0, %d)", first_layer, first_layer,
+                n_layers, cache->d.num_layers);
+  for (int32_t i = 0; i < n_layers; ++i)
+    if (ll_status s = check_commit(cache, first_layer + i, k[i], v[i])) return s;
+  std::vector<ll::CommitLayer> plan;
+  try {
+    plan.reserve(size_t(n_layers));
+  } catch (...) {  // no exception crosses the C ABI
+    return fail(LL_EINVAL, "out of host memory");
+  }
+  for (int32_t i = 0; i < n_layers; ++i) plan.push_back(commit_plan(cache, first_layer + i, k[i], v[i]));
+  const ll_cache_desc& d = cache->d;
+  ll::CommitLayersArgs a;
+  a.dtype = d.dtype;
+  a.fp4 = d.kv_format == LL_KV_FP4;
+  a.H = d.num_heads;
+  a.D = d.head_dim;
+  a.T = d.tokens_per_frame;
+  a.C = d.chunk_frames;
+  a.W = d.window_frames;
+  a.slots = slots_of(cache);
+  a.n_layers = n_layers;
+  a.layers = plan.data();
+  char msg[256] = "";
+  if (ll_status s = device_status(ll::launch_commit_layers(a, stream, msg), "commit launch", msg))
+    return s;
+  for (int32_t i = 0; i < n_layers; ++i) cache->frames[first_layer + i] += d.chunk_frames;
   return ok();
 }
 
