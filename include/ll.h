@@ -123,6 +123,21 @@ ll_status ll_cache_new_shot(ll_cache* cache, int32_t layer);
 ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const void* k,
                         const void* v, void* o, void* stream);
 
+/* ll_attn_chunk for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same computation and
+ * the same schedule (bit-identical o), but the split schedule's workspace (per-block arrival
+ * counters and partial-result slots) is a static device array inside the library instead of
+ * the workspace part of the cache's memory. The array holds 65,536 counters and 512 slots of
+ * 135,168 bytes (69.5 MB per device, resident while the library is loaded); a cache whose
+ * split schedule needs more (ll_cache_size's counters and slots) gets LL_EINVAL with a
+ * message, before anything is enqueued. The first call on a device looks the array up and
+ * clears its counters (a kernel on `stream`); every launch leaves them at zero again. The
+ * call allocates nothing, host or device. All calls on one device share the array: calls that
+ * overlap on one device (different streams, or different threads without ordering) race and
+ * give undefined results. Errors otherwise as ll_attn_chunk. */
+ll_status ll_attn_chunk_noalloc(ll_cache* cache, int32_t layer, const void* q, const void* k,
+                                const void* v, void* o, void* stream);
+
 /* ll_attn_chunk plus the chunk's text cross-attention in the same launch. In every DiT block
  * of the generator the self-attention over the frames is followed by a cross-attention of the
  * same tokens to the prompt's text tokens ("LongLive" summary page, 方法 §1 KV 重缓存, which

@@ -17,7 +17,7 @@ STATUS_NAMES = {0: "LL_OK", 1: "LL_EINVAL", 2: "LL_ESTATE", 3: "LL_EUNSUPPORTED"
 
 # every symbol include/ll.h declares
 SYMBOLS = ["ll_cache_size", "ll_cache_create", "ll_cache_destroy", "ll_cache_reset",
-           "ll_cache_new_shot", "ll_attn_chunk", "ll_attn_chunk_cross", "ll_cache_commit",
+           "ll_cache_new_shot", "ll_attn_chunk", "ll_attn_chunk_noalloc", "ll_attn_chunk_cross", "ll_cache_commit",
            "ll_cache_commit_layers", "ll_recache", "ll_kv_quant",
            "ll_cache_state", "ll_cache_export", "ll_last_error"]
 
@@ -54,6 +54,7 @@ def _declare(lib):
     lib.ll_cache_reset.argtypes = [_P]
     lib.ll_cache_new_shot.argtypes = [_P, _I32]
     lib.ll_attn_chunk.argtypes = [_P, _I32, _P, _P, _P, _P, _P]
+    lib.ll_attn_chunk_noalloc.argtypes = [_P, _I32, _P, _P, _P, _P, _P]
     lib.ll_attn_chunk_cross.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P]
     lib.ll_cache_commit.argtypes = [_P, _I32, _P, _P, _P]
     lib.ll_cache_commit_layers.argtypes = [_P, _I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P), _P]
@@ -89,6 +90,7 @@ def load_fake():
     f = _declare(ctypes.CDLL(FAKE_PATH))
     f.llfake_reset.argtypes = []
     f.llfake_fail_next.argtypes = [ctypes.c_int]
+    f.llfake_set_cus.argtypes = [ctypes.c_int]
     f.llfake_count.restype = ctypes.c_int
     f.llfake_record.argtypes = [ctypes.c_int, ctypes.POINTER(_I64)]
     f.llfake_record.restype = ctypes.c_int

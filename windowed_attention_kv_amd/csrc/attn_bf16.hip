@@ -38,6 +38,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "launch.h"
 
@@ -1094,6 +1095,46 @@ int launch_t(const Params& p, int grid, hipStream_t stream, char* err) {
 }
 
 }  // namespace
+
+// ---- the static split-schedule workspace (no allocation on the caller's side) ----
+// One copy per device, resident while the library is loaded: 256 KB of arrival counters and
+// 512 piece-state slots of 135,168 bytes (69.5 MB in all), enough for the split schedule of
+// any call on a device of up to 256 compute units.
+static __device__ __align__(256) uint8_t scratch[kStaticWsBytes];
+static_assert(kStaticWsCounters * 4 == 256 * 1024, "counter region size");
+
+namespace {
+struct StaticWs {
+  static constexpr int kMaxDevices = 64;
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+};
+StaticWs g_static_ws;
+}  // namespace
+
+int static_workspace(void** ptr, void* stream, char* err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= StaticWs::kMaxDevices) {
+    snprintf(err, 256, "no usable current device for the static workspace");
+    return 1;
+  }
+  std::lock_guard<std::mutex> lock(g_static_ws.mu);
+  if (!g_static_ws.ptr[dev]) {
+    // the symbol's device address on this device (the array's name is only a host-side
+    // stand-in); then clear the counters once, with a kernel: every split launch leaves the
+    // counters it used at zero again
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      snprintf(err, 256, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return 1;
+    }
+    if (int r = launch_zero(p, kStaticWsCounters * 4, stream, err)) return r;
+    g_static_ws.ptr[dev] = p;
+  }
+  *ptr = g_static_ws.ptr[dev];
+  return 0;
+}
 
 int launch_attention_bf16(const AttnArgs& a, void* stream, char* err) {
   constexpr int NW = 4;

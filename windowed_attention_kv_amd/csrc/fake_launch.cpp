@@ -87,7 +87,15 @@ int launch_zero(void* p, int64_t bytes, void*, char* err) {
   return 0;
 }
 
-int device_cu_count() { return 256; }
+int g_fake_cus = 256;
+int device_cu_count() { return g_fake_cus; }
+
+// a recorded stand-in address for the static workspace (never dereferenced)
+int static_workspace(void** ptr, void*, char* err) {
+  if (maybe_fail(err)) return 1;
+  *ptr = reinterpret_cast<void*>(uintptr_t(1) << 40);
+  return 0;
+}
 
 }  // namespace ll
 
@@ -99,6 +107,9 @@ void llfake_reset(void) {
 }
 
 void llfake_fail_next(int n) { g_fail = n; }
+
+// compute units the recording backend reports for caches created afterwards
+void llfake_set_cus(int n) { ll::g_fake_cus = n; }
 
 int llfake_count(void) { return int(g_log.size()); }
 

@@ -137,6 +137,17 @@ struct ExportArgs {
   uint8_t* v_out_scales = nullptr;
 };
 
+// The library's own split-schedule workspace, for callers that cannot allocate: a static
+// device array of kStaticWsBytes holding kStaticWsCounters 32-bit arrival counters (a
+// kStaticWsCounters * 4-byte region, as split_slots_offset lays it out) and then
+// kStaticWsSlots piece-state slots. static_workspace() returns its address on the current
+// device (looked up once per device) and, the first time on a device, clears its counters with
+// a kernel on `stream`.
+constexpr int64_t kStaticWsCounters = 65536;
+constexpr int64_t kStaticWsSlots = 512;
+constexpr int64_t kStaticWsBytes = kStaticWsCounters * 4 + kStaticWsSlots * kSplitSlotBytes;
+int static_workspace(void** ptr, void* stream, char* err);
+
 // Each launcher returns 0 on success or a nonzero code, with a message in `err`
 // (at least 256 bytes).
 int launch_attention(const AttnArgs& a, void* stream, char* err);

@@ -339,10 +339,13 @@ ll_status ll_cache_new_shot(ll_cache* cache, int32_t layer) {
 
 namespace {
 
-// chunk attention, optionally with the fused text cross-attention (qx != nullptr)
+// chunk attention, optionally with the fused text cross-attention (qx != nullptr); with
+// static_ws the split schedule's workspace is the library's static device array instead of
+// the cache's own
 ll_status attn_chunk_impl(ll_cache* cache, int32_t layer, const void* q, const void* k,
                           const void* v, void* o, const void* qx, const void* k_text,
-                          const void* v_text, int32_t n_text, void* ox, void* stream) {
+                          const void* v_text, int32_t n_text, void* ox, void* stream,
+                          bool static_ws = false) {
   if (ll_status s = check_layer(cache, layer)) return s;
   if (ll_status s = check_ptr(q, "q")) return s;
   if (ll_status s = check_ptr(k, "k")) return s;
@@ -369,7 +372,19 @@ ll_status attn_chunk_impl(ll_cache* cache, int32_t layer, const void* q, const v
   a.seg[1] = input_segment(d, k, v, n);
   a.scale = cache->scale;
   char msg[256] = "";
-  if (cache->L.ws_bytes) {
+  if (cache->L.ws_bytes && static_ws) {
+    if (cache->L.ws_blocks > ll::kStaticWsCounters || cache->L.ws_slots > ll::kStaticWsSlots)
+      return fail(LL_EINVAL,
+                  "the split schedule of this cache needs %d counters and %d piece slots; the "
+                  "static workspace holds %lld and %lld", cache->L.ws_blocks, cache->L.ws_slots,
+                  (long long)ll::kStaticWsCounters, (long long)ll::kStaticWsSlots);
+    void* ws = nullptr;
+    if (ll_status s = device_status(ll::static_workspace(&ws, stream, msg), "static workspace", msg))
+      return s;
+    a.ws = ws;
+    a.ws_blocks = int32_t(ll::kStaticWsCounters);
+    a.ws_slots = int32_t(ll::kStaticWsSlots);
+  } else if (cache->L.ws_bytes) {
     uint8_t* ws = cache->mem + cache->L.layer_bytes * size_t(d.num_layers);
     if (!cache->ws_ready) {
       if (ll_status s = device_status(
@@ -398,6 +413,12 @@ extern "C" {
 ll_status ll_attn_chunk(ll_cache* cache, int32_t layer, const void* q, const void* k,
                         const void* v, void* o, void* stream) {
   return attn_chunk_impl(cache, layer, q, k, v, o, nullptr, nullptr, nullptr, 0, nullptr, stream);
+}
+
+ll_status ll_attn_chunk_noalloc(ll_cache* cache, int32_t layer, const void* q, const void* k,
+                                const void* v, void* o, void* stream) {
+  return attn_chunk_impl(cache, layer, q, k, v, o, nullptr, nullptr, nullptr, 0, nullptr, stream,
+                         true);
 }
 
 ll_status ll_attn_chunk_cross(ll_cache* cache, int32_t layer, const void* q, const void* k,
