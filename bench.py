@@ -1,14 +1,19 @@
 """Benchmark of the window+sink chunk-attention hot path on one MI355X.
 
-One step = one pass of the layer workload (12 heads x 128, 1560 tokens/frame, chunk 3
-frames = 4680 query rows, sink 3 + window 9 frames, 20 chunks streamed from an empty cache):
-for each chunk, ll_attn_chunk then ll_cache_commit. Inputs are synthetic bf16 N(0, 0.25),
-generated on the GPU before timing (resident in HBM). Prints ONE JSON line.
+One step = one pass of the stack workload: 30 layers of 12 heads x 128 (1560 tokens/frame,
+chunk 3 frames = 4680 query rows, sink 3 + window 9 frames), 80 chunks streamed from an empty
+cache, 4 denoise steps per chunk; every denoise step runs ll_attn_chunk on each of the 30
+layers, and after the last step one ll_cache_commit_layers commits the chunk's K/V into all
+30 layers. Inputs are synthetic bf16 N(0, 0.25), generated on the GPU before timing (resident
+in HBM) and cycled through a pool of 8 sets (values do not change the work). Prints ONE JSON
+line.
 
-value = query rows attended per second over the whole step (attention + commit);
-roofline = the attention kernel against the bf16 dense MFMA peak, from HIP events recorded on
-the launch stream around every attention launch inside the timed region; extra rows report
-the commit, the FP4 path and the recache, each timed on its own after the main loop.
+value = query rows attended per second over the whole step (attention + commits);
+roofline = the attention kernel against the bf16 dense MFMA peak: average algorithmic flops
+per launch over the pass, divided by the average launch duration from HIP events recorded on
+the launch stream around each chunk's 120 attention launches in the timed region; extra rows
+report the single-layer stream, the commits, the FP4 store, the recache and the other
+workloads, each timed on its own after the main loop.
 """
 from __future__ import annotations
 
@@ -28,8 +33,8 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E (published)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the FP4 / recache rows")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -144,92 +149,180 @@ def run_stream(cache, inputs, timer=None):
 _OUT = [None]
 
 
-def cpu_baseline(shape):
-    """The fp64 oracle on a bounded sample of the same workload: the whole 20-chunk stream
-    (fill-up and steady chunks, attention and commit, inputs drawn beforehand) for 2 of the 12
-    heads and all 4680 rows of each chunk, scaled to 12 heads (heads are independent and cost
-    the same)."""
-    from oracle.model import LayerModel
-    from windowed_attention_kv_amd import synth
+def host_cores():
+    """Host CPU counts of the machine the oracle runs on: logical CPUs, CPUs this process may
+    use, and physical cores from lscpu (None where unavailable)."""
+    import subprocess
+    info = {"logical_cpus": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0))}
+    try:
+        out = subprocess.run(["lscpu", "-p=CORE,SOCKET"], capture_output=True, text=True,
+                             timeout=10).stdout
+        cores = {tuple(l.split(",")) for l in out.splitlines() if l and not l.startswith("#")}
+        info["physical_cores_lscpu"] = len(cores) or None
+        model = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in model.splitlines():
+            if line.startswith("Model name:"):
+                info["model"] = line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        info["physical_cores_lscpu"] = None
+    return info
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
-    Hs = 2
-    sub = synth.shrink(shape, heads=Hs)
-    m = LayerModel(sub.sink_frames, sub.window_frames, sub.chunk_frames, sub.tokens_per_frame,
-                   Hs, sub.head_dim)
-    inputs = [synth.chunk_inputs(sub, 0, 0, c) for c in range(shape.chunks)]
+        return None
+
+
+def cpu_baseline(shape):
+    """The fp64 oracle as it stands, timed on bounded samples of the workloads (input drawing
+    excluded), each scaled to its whole workload by algorithmic flops or by heads (every
+    steady chunk, head and layer does the same work):
+      - the stack (the headline): layer 0, 4 denoise steps, chunks 0-7 (fill-up and steady
+        chunks, attention and commit), 1 of 12 heads, scaled by flops to 30 layers x 80 chunks
+        x 12 heads;
+      - the tiny config in full; the FP4 stack (1 denoise step of chunks 0-7 over an FP4
+        store, codec included, 1 head, scaled by flops); one layer of the prompt-switch recache
+        (1 head, scaled by heads); one steady chunk call (23,400 keys, 1 head) on 1 thread."""
+    from oracle.model import LayerModel
+    from windowed_attention_kv_amd import synth
+    n, T, C, S, W = shape.n_query, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames, shape.window_frames
+    L, steps, chunks = 30, 4, 80
+    D = shape.head_dim
+
+    def flops(chunk_ids, heads, n_steps):
+        return sum(n_steps * n * visible_keys(c, C, S, W, T) * heads * 4 * D for c in chunk_ids)
+
+    sub1 = synth.shrink(shape, heads=1)
+    stack_flops = L * flops(range(chunks), shape.heads, steps)
+    # the stack: layer 0, 4 steps, chunks 0-7, 1 head
+    sub_chunks = 8
+    ins = [[synth.chunk_inputs(sub1, 0, st, c) for st in range(steps)] for c in range(sub_chunks)]
+    m = LayerModel(S, W, C, T, 1, D)
     t0 = time.perf_counter()
-    for q, k, v in inputs:
-        m.attn_chunk(q.values, k.values, v.values)
+    for c in range(sub_chunks):
+        for st in range(steps):
+            q, k, v = ins[c][st]
+            m.attn_chunk(q.values, k.values, v.values)
         m.commit(k.values, v.values)
     dt = time.perf_counter() - t0
-    stream_time = dt * shape.heads / Hs
+    sub_flops = flops(range(sub_chunks), 1, steps)
+    stack_s = dt * stack_flops / sub_flops
+    rows_stack = n * L * steps * chunks
     extra = {}
-    # the same stream over the oracle's FP4 store (codec included), for 1 of the 12 heads
-    sub1 = synth.shrink(shape, heads=1)
-    m4 = LayerModel(sub1.sink_frames, sub1.window_frames, sub1.chunk_frames,
-                    sub1.tokens_per_frame, 1, sub1.head_dim, kv_format="fp4")
-    inputs1 = [synth.chunk_inputs(sub1, 0, 0, c) for c in range(shape.chunks)]
+    # the tiny config, whole stream
+    tiny = synth.CONFIGS["tiny"]
+    tins = [synth.chunk_inputs(tiny, 0, 0, c) for c in range(tiny.chunks)]
+    mt = LayerModel(tiny.sink_frames, tiny.window_frames, tiny.chunk_frames, tiny.tokens_per_frame,
+                    tiny.heads, tiny.head_dim)
     t0 = time.perf_counter()
-    for q, k, v in inputs1:
+    for q, k, v in tins:
+        mt.attn_chunk(q.values, k.values, v.values)
+        mt.commit(k.values, v.values)
+    dtt = time.perf_counter() - t0
+    extra["tiny_config"] = {"value": round(tiny.n_query * tiny.chunks / dtt, 1), "unit": "query-tokens/s",
+                            "sample": f"the whole 8-chunk fp32 stream, {dtt:.3f} s measured"}
+    # FP4 stack: 1 step of chunks 0-7 over an FP4 store (codec included), 1 head
+    m4 = LayerModel(S, W, C, T, 1, D, kv_format="fp4")
+    t0 = time.perf_counter()
+    for c in range(sub_chunks):
+        q, k, v = ins[c][steps - 1]
         m4.attn_chunk(q.values, k.values, v.values)
         m4.commit(k.values, v.values, k.bits, v.bits)
     dt4 = time.perf_counter() - t0
-    extra["fp4_stream"] = {"value": round(shape.n_query * shape.chunks / (dt4 * shape.heads), 3),
-                           "unit": "query-tokens/s",
-                           "sample": f"the {shape.chunks}-chunk stream over an FP4 store, 1/{shape.heads} heads, "
-                                     f"{dt4:.1f} s measured, scaled by heads"}
+    fp4_s = dt4 * stack_flops / flops(range(sub_chunks), 1, 1)
+    extra["fp4_stack"] = {"value": round(rows_stack / fp4_s, 1), "unit": "query-tokens/s",
+                          "sample": (f"1 denoise step of chunks 0-{sub_chunks - 1} over an FP4 store "
+                                     f"(codec included), layer 0, 1/{shape.heads} heads, {dt4:.1f} s "
+                                     "measured, scaled by flops to the FP4 stack")}
     # one layer of the prompt-switch recache (12 held frames, 512 text tokens), 1 head
-    mr = LayerModel(sub1.sink_frames, sub1.window_frames, sub1.chunk_frames,
-                    sub1.tokens_per_frame, 1, sub1.head_dim)
-    for q, k, v in inputs1[:4]:
-        mr.commit(k.values, v.values)
-    rows = len(mr.held()) * sub1.tokens_per_frame
+    mr = LayerModel(S, W, C, T, 1, D)
+    for c in range(4):
+        mr.commit(ins[c][0][1].values, ins[c][0][2].values)
+    rows = len(mr.held()) * T
     rin = synth.recache_inputs(sub1, 0, rows, 512)
     t0 = time.perf_counter()
     mr.recache(*(x.values for x in rin))
     dtr = time.perf_counter() - t0
-    extra["recache_30_layers"] = {"value": round(rows / (dtr * shape.heads), 3),
+    extra["recache_30_layers"] = {"value": round(rows / (dtr * shape.heads), 1),
                                   "unit": "query-tokens/s",
-                                  "sample": f"one layer's recache ({rows} rows: block-causal self + 512-key "
-                                            f"cross), 1/{shape.heads} heads, {dtr:.1f} s measured, "
-                                            "scaled by heads (30 layers: the same rate)"}
-    return {"value": round(shape.n_query * shape.chunks / stream_time, 3), "unit": "query-tokens/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 oracle, the whole {shape.chunks}-chunk stream (attention + commit) "
-                       f"for {Hs}/{shape.heads} heads x {shape.n_query} rows, {dt:.1f} s measured, "
-                       f"scaled by heads to {shape.heads}"),
-            "other_workloads": extra}
+                                  "sample": (f"one layer's recache ({rows} rows: block-causal self + 512-key "
+                                             f"cross), 1/{shape.heads} heads, {dtr:.1f} s measured, "
+                                             "scaled by heads (30 layers: the same rate)")}
+    # one steady chunk call on one thread, 1 head
+    q, k, v = ins[sub_chunks - 1][0]
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            m.attn_chunk(q.values, k.values, v.values)
+            dt1 = time.perf_counter() - t0
+        single = {"value": round(n / (dt1 * shape.heads), 1), "unit": "query-tokens/s", "cores": 1,
+                  "sample": (f"one steady chunk call (4680 rows x 23,400 keys), 1/{shape.heads} heads, "
+                             f"BLAS limited to 1 thread, {dt1:.1f} s measured, scaled by heads")}
+    except Exception as e:  # threadpoolctl missing: the leg is reported as not run
+        single = {"value": None, "note": f"not run: {e}"}
+    extra["steady_call_1_thread"] = single
+    threads = _blas_threads()
+    return {"value": round(rows_stack / stack_s, 1), "unit": "query-tokens/s",
+            "cores": threads if threads else os.cpu_count(), "kind": "oracle",
+            "sample": (f"fp64 oracle on the stack: layer 0, {steps} denoise steps, chunks 0-{sub_chunks - 1} "
+                       f"(attention + commit), 1/{shape.heads} heads x {n} rows, {dt:.1f} s measured "
+                       f"({sub_flops / 1e12:.2f} TFLOP), scaled by algorithmic flops to the whole stack "
+                       f"({stack_flops / 1e15:.3f} PFLOP): {stack_s / 3600:.1f} h"),
+            "cores_note": "BLAS threads the oracle's matrix products used (threadpoolctl)",
+            "host": host_cores(), "other_workloads": extra}
 
 
-def stack_row(torch, shape, Cache, attn_flops, kv_format, pool):
-    """The stack workload: L layers x 4 denoise steps x 80 chunks (only the last step of a
-    chunk commits), one pass from an empty cache. Inputs cycle through a pool of resident
-    synthetic sets (values do not change the work). Timed as a whole with events."""
-    L, steps, chunks = 30, 4, 80
-    n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
-    C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
-    cache = Cache(L, H, D, T, C, S, W, kv_format=kv_format)
-    out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
-    flops = 0.0
-    for c in range(chunks):
-        flops += L * steps * attn_flops(n, visible_keys(c, C, S, W, T), H, D)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
+def stack_pass(cache, pool, out, L, steps, chunks, timer=None):
+    """One pass of the stack workload on `cache`: per chunk, 4 denoise steps of attention
+    over the L layers, then one batched commit of the last step's K/V into all layers.
+    Inputs cycle through `pool`. With a timer, each chunk's attention launches and its
+    commit launch are bracketed by events."""
     i = 0
     for c in range(chunks):
+        if timer:
+            s = timer.start()
+        last_k, last_v = [], []
         for st in range(steps):
             for layer in range(L):
                 q, k, v = pool[i % len(pool)]
                 i += 1
                 cache.attn_chunk(layer, q, k, v, out=out)
                 if st == steps - 1:
-                    cache.commit(layer, k, v)
+                    last_k.append(k)
+                    last_v.append(v)
+        if timer:
+            timer.stop(s, "attn")
+            s = timer.start()
+        cache.commit_layers(0, last_k, last_v)
+        if timer:
+            timer.stop(s, "commit")
+
+
+def stack_flops(shape, attn_flops, L=30, steps=4, chunks=80):
+    n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
+    C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
+    return sum(L * steps * attn_flops(n, visible_keys(c, C, S, W, T), H, D) for c in range(chunks))
+
+
+def stack_row(torch, shape, Cache, attn_flops, kv_format, pool):
+    """One pass of the stack workload from an empty cache with the given KV store, timed as
+    a whole with events."""
+    L, steps, chunks = 30, 4, 80
+    n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
+    C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
+    cache = Cache(L, H, D, T, C, S, W, kv_format=kv_format)
+    out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+    flops = stack_flops(shape, attn_flops)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    stack_pass(cache, pool, out, L, steps, chunks)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1)
@@ -238,7 +331,7 @@ def stack_row(torch, shape, Cache, attn_flops, kv_format, pool):
             "tflops": round(flops / ms / 1e9, 1),
             "frac_bf16_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
             "pflop": round(flops / 1e15, 4),
-            "work": f"{L} layers x {steps} steps x {chunks} chunks, {kv_format} KV, attention + commits"}
+            "work": f"{L} layers x {steps} steps x {chunks} chunks, {kv_format} KV, attention + batched commits"}
 
 
 def composite_row(torch, shape, Cache, attn_flops, pool):
@@ -277,13 +370,16 @@ def composite_row(torch, shape, Cache, attn_flops, pool):
             for layer in range(L):
                 cache.recache(layer, big[0][:held], big[1][:held], big[2][:held], big[3][:held],
                               txt[0], txt[1], out=o[:held], out_x=ox[:held])
+        last_k, last_v = [], []
         for st in range(steps):
             for layer in range(L):
                 q, k, v = pool[i % len(pool)]
                 i += 1
                 cache.attn_chunk(layer, q, k, v, out=out)
                 if st == steps - 1:
-                    cache.commit(layer, k, v)
+                    last_k.append(k)
+                    last_v.append(v)
+        cache.commit_layers(0, last_k, last_v)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1)
@@ -300,27 +396,33 @@ def composite_row(torch, shape, Cache, attn_flops, pool):
             "tflops": round(flops / ms / 1e9, 1),
             "frac_bf16_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
             "pflop": round(flops / 1e15, 4), "switches_at_chunk": switches,
-            "work": (f"{L} layers x {steps} steps x {chunks} chunks, dense KV, attention + commits, "
+            "work": (f"{L} layers x {steps} steps x {chunks} chunks, dense KV, attention + batched commits, "
                      f"{len(switches)} prompt switches each recaching {L} layers ({n_text} text tokens)")}
 
 
-def commit_batch_row(torch, shape, Cache, kv_format, k, v):
-    """Per-commit time of 30 back-to-back steady commits (one per layer of a 30-layer cache),
-    the pattern of the stack workload; events bracket each batch of 30."""
+def commit_batch_row(torch, shape, Cache, kv_format, pairs, batched=False):
+    """Per-layer commit time of 30 steady commits (one per layer of a 30-layer cache), either
+    30 back-to-back ll_cache_commit calls or one ll_cache_commit_layers call for all 30
+    layers (the stack workload's pattern). Every layer commits its own K/V pair (30 distinct
+    pairs, 862 MB: more than the caches hold, as in the stack); events bracket each batch."""
     L = 30
     n, H, D = shape.n_query, shape.heads, shape.head_dim
     cache = Cache(L, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
                   shape.window_frames, kv_format=kv_format)
+    ks, vs = [p[0] for p in pairs[:L]], [p[1] for p in pairs[:L]]
     # warm every layer past the commit that moves the sink frames out of the window (timed
     # in its own row), so each timed commit is a steady-state one
     for _ in range(shape.window_frames // shape.chunk_frames + 1):
         for layer in range(L):
-            cache.commit(layer, k, v)
+            cache.commit(layer, ks[layer], vs[layer])
     tm = EventTimer(torch)
     for rep in range(10):
         s = tm.start()
-        for layer in range(L):
-            cache.commit(layer, k, v)
+        if batched:
+            cache.commit_layers(0, ks, vs)
+        else:
+            for layer in range(L):
+                cache.commit(layer, ks[layer], vs[layer])
         tm.stop(s, "batch")
     torch.cuda.synchronize()
     ms = tm.totals()["batch"][0] / (10 * L)
@@ -333,23 +435,24 @@ def commit_batch_row(torch, shape, Cache, kv_format, k, v):
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def copy_ceiling_row(torch, k, v):
-    """Context for the commit rows: a plain device copy (torch's copy kernel) of the same K and V
-    a dense commit moves, 2 x 14.38 MB read and written; per-copy time of 30 back-to-back pairs
-    of copies, events bracketing each batch like commit_batch_row."""
-    dk, dv = torch.empty_like(k), torch.empty_like(v)
-    for _ in range(3):
+def copy_ceiling_row(torch, pairs):
+    """Context for the commit rows: a plain device copy (torch's copy kernel) of the bytes the
+    batched commit moves: 30 distinct K/V pairs (2 x 14.38 MB each) copied back to back into
+    30 destination pairs; per-pair time, events bracketing each batch of 30."""
+    dst = [(torch.empty_like(k), torch.empty_like(v)) for k, v in pairs]
+    for (k, v), (dk, dv) in zip(pairs, dst):
         dk.copy_(k)
         dv.copy_(v)
     tm = EventTimer(torch)
     for rep in range(10):
         s = tm.start()
-        for _ in range(30):
+        for (k, v), (dk, dv) in zip(pairs, dst):
             dk.copy_(k)
             dv.copy_(v)
         tm.stop(s, "batch")
     torch.cuda.synchronize()
-    ms = tm.totals()["batch"][0] / (10 * 30)
+    ms = tm.totals()["batch"][0] / (10 * len(pairs))
+    k = pairs[0][0]
     nbytes = 2 * 2 * k.numel() * k.element_size()
     gbs = nbytes / ms / 1e6
     return {"us_per_pair": round(ms * 1e3, 3), "bytes": nbytes, "gbs": round(gbs, 1),
@@ -425,10 +528,17 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     n, H, D = shape.n_query, shape.heads, shape.head_dim
     inputs = gen_inputs(torch, shape.chunks, n, H, D, 7, "cuda")
     out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
-    res["commit_30_layers"] = commit_batch_row(torch, shape, Cache, "dense", inputs[0][1], inputs[0][2])
-    res["fp4_commit_30_layers"] = commit_batch_row(torch, shape, Cache, "fp4", inputs[0][1], inputs[0][2])
+    res["layer_stream"] = layer_stream_row(torch, shape, Cache, attn_flops, inputs)
+    # 30 distinct (K, V) pairs for the commit rows (the 20 chunks' q, k, v tensors, paired up)
+    flat = [t for trip in inputs for t in trip]
+    pairs = [(flat[2 * i], flat[2 * i + 1]) for i in range(30)]
+    res["commit_layers_30_dense"] = commit_batch_row(torch, shape, Cache, "dense", pairs, batched=True)
+    res["commit_layers_30_fp4"] = commit_batch_row(torch, shape, Cache, "fp4", pairs, batched=True)
+    res["commit_30_layers"] = commit_batch_row(torch, shape, Cache, "dense", pairs)
+    res["fp4_commit_30_layers"] = commit_batch_row(torch, shape, Cache, "fp4", pairs)
     res["spill_commit_30_layers"] = spill_commit_row(torch, shape, Cache, inputs[0][1], inputs[0][2])
-    res["plain_copy_same_bytes"] = copy_ceiling_row(torch, inputs[0][1], inputs[0][2])
+    res["plain_copy_same_bytes"] = copy_ceiling_row(torch, pairs)
+    del pairs, flat
     res["kv_quant_same_bytes_as_fp4_commit"] = quant_chunk_row(torch, inputs[0][1], inputs[0][2])
     # FP4 KV store at the layer shape: steady-state attention (15 visible frames)
     c4 = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
@@ -564,10 +674,63 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
                                 "note": "per layer: block-causal self + cross (512 text keys) + slot rewrite"}
     del cr, big, txt, o, ox
     pool = gen_inputs(torch, 8, n, H, D, 21, "cuda")
-    res["stack_dense"] = stack_row(torch, shape, Cache, attn_flops, "dense", pool)
     res["stack_fp4"] = stack_row(torch, shape, Cache, attn_flops, "fp4", pool)
     res["interactive_composite"] = composite_row(torch, shape, Cache, attn_flops, pool)
+    res["gemm_bf16_ceiling"] = gemm_ceiling_row(torch)
     return res
+
+
+def layer_stream_row(torch, shape, Cache, attn_flops, inputs, passes=5):
+    """The single-layer workload: 20 chunks streamed from an empty 1-layer cache, each chunk
+    ll_attn_chunk then ll_cache_commit; events around every attention and commit launch."""
+    n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
+    C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
+    cache = Cache(1, H, D, T, C, S, W)
+    _OUT[0] = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+    run_stream(cache, inputs)
+    torch.cuda.synchronize()
+    timer = EventTimer(torch)
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        cache.reset()
+        run_stream(cache, inputs, timer)
+    torch.cuda.synchronize()
+    ms_pass = (time.perf_counter() - t0) * 1e3 / passes
+    tot = timer.totals()
+    flops = sum(attn_flops(n, visible_keys(c, C, S, W, T), H, D) for c in range(shape.chunks))
+    attn_ms = tot["attn"][0] / tot["attn"][1]
+    commit_ms = tot["commit"][0] / tot["commit"][1]
+    commit_bytes = 2 * 2 * n * H * D * 2
+    return {"ms_per_stream": round(ms_pass, 3), "query_tokens_per_s": round(n * shape.chunks / ms_pass * 1e3, 1),
+            "attention_avg_launch_ms": round(attn_ms, 4),
+            "attention_tflops": round(flops / shape.chunks / attn_ms / 1e9, 1),
+            "frac_bf16_peak": round(flops / shape.chunks / attn_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "commit_avg_launch_ms": round(commit_ms, 5),
+            "commit_frac_hbm": round(commit_bytes / commit_ms / 1e6 / HBM_PEAK_GBS, 4),
+            "work": "1 layer, 20 chunks streamed from an empty cache (attention + commit per chunk)"}
+
+
+def gemm_ceiling_row(torch, m=8192):
+    """Context for the attention roofline: a plain bf16 GEMM (torch.matmul, the vendor BLAS)
+    of m x m x m on the same device, its sustained rate and fraction of the dense bf16 peak."""
+    a = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    b = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    c = torch.empty((m, m), device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * m ** 3 / ms / 1e9
+    return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "note": f"torch.matmul bf16 {m}x{m}x{m}: the vendor GEMM's sustained rate on this device"}
 
 
 def main():
@@ -583,18 +746,21 @@ def main():
     import torch
     from windowed_attention_kv_amd import Cache, attn_flops, kv_quant, synth
 
-    shape = synth.CONFIGS["layer"]
+    layer_shape = synth.CONFIGS["layer"]
+    shape = synth.CONFIGS["stack"]
+    L, steps, chunks = shape.layers, shape.steps, shape.chunks
     n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
     C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
     torch.cuda.set_device(0)
-    inputs = gen_inputs(torch, shape.chunks, n, H, D, 1234, "cuda")
-    _OUT[0] = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
-    cache = Cache(1, H, D, T, C, S, W)
-    flops_step = sum(attn_flops(n, visible_keys(c, C, S, W, T), H, D) for c in range(shape.chunks))
+    pool = gen_inputs(torch, 8, n, H, D, 1234, "cuda")
+    out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+    cache = Cache(L, H, D, T, C, S, W)
+    flops_step = stack_flops(shape, attn_flops, L, steps, chunks)
+    launches = L * steps * chunks
 
     for _ in range(args.warmup):
         cache.reset()
-        run_stream(cache, inputs)
+        stack_pass(cache, pool, out, L, steps, chunks)
     torch.cuda.synchronize()
 
     timer = EventTimer(torch)
@@ -602,34 +768,40 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         cache.reset()
-        run_stream(cache, inputs, timer)
+        stack_pass(cache, pool, out, L, steps, chunks, timer)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tot = timer.totals()
     ms_step = wall * 1e3 / args.steps
-    attn_ms = tot["attn"][0] / tot["attn"][1]            # average attention launch
-    attn_flops_launch = flops_step / shape.chunks          # average algorithmic flops per launch
+    # average attention launch: each chunk's 120 back-to-back attention launches are bracketed
+    # by one pair of events, so the launch gaps between them are included
+    attn_ms = tot["attn"][0] / (launches * args.steps)
+    attn_flops_launch = flops_step / launches              # average algorithmic flops per launch
     achieved = attn_flops_launch / attn_ms / 1e9           # TFLOP/s
-    commit_ms = tot["commit"][0] / tot["commit"][1]
-    commit_bytes = 2 * 2 * n * H * D * 2                   # read + write of K and V
+    commit_ms = tot["commit"][0] / tot["commit"][1]        # one batched commit of 30 layers
+    commit_bytes = L * 2 * 2 * n * H * D * 2               # read + write of K and V, every layer
+    rows_step = n * launches
 
     line = {
         "metric": "query-tokens/s and TFLOP/s for window+sink chunk attention (% bf16 MFMA peak)",
-        "value": round(n * shape.chunks / (ms_step / 1e3), 1),
+        "value": round(rows_step / (ms_step / 1e3), 1),
         "unit": "query-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(ms_step, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "layer: 12 heads x 128, 1560 tok/frame, chunk 3 (4680 q), sink 3, "
-                               "window 9, 20 chunks streamed (attn + commit per chunk)",
-                   "query_rows_per_step": n * shape.chunks,
-                   "attention_tflop_per_step": round(flops_step / 1e12, 4),
+        "config": {"workload": (f"stack: {L} layers x {steps} denoise steps x {chunks} chunks streamed from an "
+                                "empty cache; per layer 12 heads x 128, 1560 tok/frame, chunk 3 frames (4680 "
+                                "query rows), sink 3 + window 9 frames; chunk attention for every step and "
+                                "layer, one batched commit of all layers per chunk"),
+                   "query_rows_per_step": rows_step,
+                   "attention_launches_per_step": launches,
+                   "attention_pflop_per_step": round(flops_step / 1e15, 4),
                    "tflops_whole_step": round(flops_step / (ms_step / 1e3) / 1e12, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -642,14 +814,17 @@ def main():
                      "kernel": "attn_bf16_direct_kernel<8,2,false,false>",
                      "avg_launch_ms": round(attn_ms, 4),
                      "avg_flops_per_launch": attn_flops_launch},
-        "rows": {"commit": {"avg_launch_ms": round(commit_ms, 5), "bytes": commit_bytes,
-                            "gbs": round(commit_bytes / commit_ms / 1e6, 1),
-                            "frac_hbm": round(commit_bytes / commit_ms / 1e6 / HBM_PEAK_GBS, 4)}},
+        "rows": {"commit_layers_in_stack": {
+            "avg_launch_ms": round(commit_ms, 4), "layers_per_launch": L, "bytes": commit_bytes,
+            "us_per_layer": round(commit_ms * 1e3 / L, 3),
+            "gbs": round(commit_bytes / commit_ms / 1e6, 1),
+            "frac_hbm": round(commit_bytes / commit_ms / 1e6 / HBM_PEAK_GBS, 4)}},
     }
+    del cache
     if not args.no_extra:
-        line["rows"].update(extra_rows(torch, shape, Cache, kv_quant, attn_flops))
+        line["rows"].update(extra_rows(torch, layer_shape, Cache, kv_quant, attn_flops))
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(shape)
+        line["cpu_baseline"] = cpu_baseline(layer_shape)
     print(json.dumps(line), flush=True)
 
 

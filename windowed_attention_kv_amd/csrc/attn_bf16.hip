@@ -714,6 +714,7 @@ void attn_bf16_direct_kernel(Params p) {
     const int row0 = qblk * (NW * 32);
     const int row = row0 + wave * 32 + l32;
     const int lim = xjob ? na : row_limit(p, row < p.nq ? row : p.nq - 1);
+    const bool wave_live = row0 + wave * 32 < p.nq;   // uniform over the wave
     const int wave_min_lim = xjob ? na : row_limit(p, min(row0 + wave * 32, p.nq - 1));
     const int kend = xjob ? na : row_limit(p, min(row0 + NW * 32 - 1, p.nq - 1));
     // tiles per segment; in block-causal mode only segment A holds keys and the last visible
@@ -831,9 +832,12 @@ void attn_bf16_direct_kernel(Params p) {
       const bool inA = t < ntA;
       const int r0 = (inA ? t : t - ntA) * TR + u2 * BN;       // first row of the sub-tile
       const int seg_left = (inA ? na : nb) - r0;
-      // a sub-tile wholly past the end is skipped (FP4: computed fully masked instead, so every
-      // sub-tile reaches its share of the next tile's dequantisation and the loads after it)
-      if (!FP4 && seg_left <= 0) continue;
+      // a sub-tile wholly past the end is skipped, and so is all the work of a wave whose 32
+      // rows lie past the last query row (the ragged last block of a head: 3 of its 8 waves
+      // hold rows at the layer shape); such a wave still issues its share of every tile's
+      // loads and meets every barrier. (FP4: computed fully masked instead, so every sub-tile
+      // reaches its share of the next tile's dequantisation and the loads after it.)
+      if (!FP4 && (seg_left <= 0 || !wave_live)) continue;
       const int key0 = (inA ? 0 : na) + r0;
 
       // S^T = K Q^T: 16 MFMAs, each fed by one 16-byte LDS read. The reads run kPipe MFMAs
