@@ -14,6 +14,8 @@ def pytest_configure(config):
 
 
 def _has_gpu() -> bool:
+    if os.environ.get("LL_NO_GPU_PROBE"):   # host-only runs (the sanitizer subprocess)
+        return False
     try:
         import torch
         return torch.cuda.is_available()

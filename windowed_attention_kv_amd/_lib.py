@@ -7,7 +7,8 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libll.so")
-FAKE_PATH = os.path.join(PKG, "libll_fake.so")
+# the recording build of the host layer (another build of it, e.g. a sanitizer one, via LL_FAKE_LIB)
+FAKE_PATH = os.environ.get("LL_FAKE_LIB") or os.path.join(PKG, "libll_fake.so")
 
 LL_ABI_VERSION = 1
 LL_OK, LL_EINVAL, LL_ESTATE, LL_EUNSUPPORTED, LL_EDEVICE = range(5)

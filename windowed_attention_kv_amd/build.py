@@ -1,5 +1,5 @@
-"""Build the HIP library (libll.so, gfx950) and the CPU-only recording variant
-(libll_fake.so) in-tree. Run `python -m windowed_attention_kv_amd.build`."""
+"""Build the HIP library (libll.so, gfx950), the CPU-only recording variant (libll_fake.so)
+and its sanitizer-instrumented twin (libll_fake_san.so) in-tree. Run `python -m windowed_attention_kv_amd.build`."""
 from __future__ import annotations
 
 import os
@@ -15,6 +15,7 @@ HIP_SOURCES = ["attn_bf16.hip", "attn_f32.hip", "cache_ops.hip"]
 HOST_SOURCES = ["ll_host.cpp"]
 LIB = os.path.join(PKG, "libll.so")
 FAKE_LIB = os.path.join(PKG, "libll_fake.so")
+SAN_LIB = os.path.join(PKG, "libll_fake_san.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed-fp32 VALU ops are disabled for every HIP object (hipcc emits them on its own from
@@ -26,6 +27,10 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # NaN quieting of every fmaxf operand is dropped
 EXTRA_FLAGS = {"attn_bf16.hip": ["-fno-honor-nans"]}
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+# the recording host build again, instrumented with AddressSanitizer and UndefinedBehavior-
+# Sanitizer (host code only; tests/test_host_sanitizers.py runs the host tests against it)
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"]
 
 
 def _run(cmd):
@@ -58,6 +63,10 @@ def build(verbose: bool = False) -> None:
     _run(["g++", *HOST_FLAGS, "-shared", os.path.join(CSRC, "ll_host.cpp"),
           os.path.join(CSRC, "fake_launch.cpp"), "-o", tmp])
     shutil.move(tmp, FAKE_LIB)
+    tmp = SAN_LIB + ".tmp"
+    host_sources = [os.path.join(CSRC, "ll_host.cpp"), os.path.join(CSRC, "fake_launch.cpp")]
+    _run(["g++", *HOST_FLAGS, *SAN_FLAGS, "-shared", *host_sources, "-o", tmp])
+    shutil.move(tmp, SAN_LIB)
 
 
 if __name__ == "__main__":

@@ -110,7 +110,8 @@ __device__ __forceinline__ int32_t row_limit(const Params& p, int32_t row) {
 // FP4 -> bf16 for the 8 codes of one 32-bit word (element e in bits 4e..4e+3) with scale
 // byte sb: value = (-1)^s * grid[code & 7] * 2^(sb-127), grid = {0,.5,1,1.5,2,3,4,6}, using
 // gfx950's scaled fp4->bf16 conversion (exact: every such value is a bf16, subnormals
-// included; checked for all 256 bytes x 255 scale bytes).
+// included; every code byte at every scale byte the encoder produces, 0..252, is read back
+// through this path and checked against the oracle, in both attention kernels).
 __device__ __forceinline__ uint4 dequant8(uint32_t w, uint32_t sb) {
   const float scale = __uint_as_float(sb ? (sb << 23) : 0x00400000u);
   return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
