@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the FP4 / recache rows")
+    ap.add_argument("--row", choices=["share", "recache"], default=None,
+                    help="run only this workload (for profiling) and print its row: the 3-head "
+                         "share streams or the 30-layer recache")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -597,9 +600,38 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
         "cross_us_over_self_only": round((ms_f - res["attention_steady"]["ms"]) * 1e3, 1),
         "note": "self (23400 keys) + text cross-attention (512 keys) in one launch"}
     del qx, ktx, vtx, ox
-    # one GPU's share of the heads under 4-way sequence parallelism: the layer shape at 3
-    # heads (57 query blocks on 256 CUs, so chunk attention runs with the split schedule)
-    Hs = 3
+    res.update(share_rows(torch, shape, Cache, attn_flops, inputs))
+    # standalone quant of one 12-frame cache (K and V): 2 x 18720 x 1536 elements
+    x = torch.randn((2 * 18720 * H, D), device="cuda").mul_(0.5).to(torch.bfloat16)
+    pk = torch.empty((x.shape[0], D // 2), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((x.shape[0], D // 16), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        kv_quant(x, pk, sc)
+    tm = EventTimer(torch)
+    for _ in range(10):
+        s = tm.start()
+        kv_quant(x, pk, sc)
+        tm.stop(s, "quant")
+    torch.cuda.synchronize()
+    ms = tm.totals()["quant"][0] / 10
+    qbytes = x.numel() * 2 + pk.numel() + sc.numel()
+    res["kv_quant_12_frames"] = {"ms": round(ms, 5), "bytes": qbytes, "gbs": round(qbytes / ms / 1e6, 1),
+                                 "frac_hbm": round(qbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del x, pk, sc
+    res["recache_30_layers"] = recache_row(torch, shape, Cache, inputs)
+    pool = gen_inputs(torch, 8, n, H, D, 21, "cuda")
+    res["stack_fp4"] = stack_row(torch, shape, Cache, attn_flops, "fp4", pool)
+    res["interactive_composite"] = composite_row(torch, shape, Cache, attn_flops, pool)
+    res["gemm_bf16_ceiling"] = gemm_ceiling_row(torch)
+    return res
+
+
+def share_rows(torch, shape, Cache, attn_flops, inputs):
+    """One GPU's share of the heads under 4-way sequence parallelism: the layer shape at 3
+    heads (57 query blocks on 256 CUs, so chunk attention runs with the split schedule),
+    20-chunk streams over a dense and an FP4 cache; steady chunks timed."""
+    res = {}
+    n, D, Hs = shape.n_query, shape.head_dim, 3
     share_in = [tuple(t[:, :Hs].contiguous() for t in trip) for trip in inputs]
     outs = torch.empty((n, Hs, D), dtype=torch.bfloat16, device="cuda")
     share_flops = attn_flops(n, 23400, Hs, D)
@@ -622,24 +654,13 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
                     "note": (f"3 of 12 heads (4-way sequence-parallel share), {kv_format} cache, "
                              "split schedule")}
     del share_in, outs, cs
-    # standalone quant of one 12-frame cache (K and V): 2 x 18720 x 1536 elements
-    x = torch.randn((2 * 18720 * H, D), device="cuda").mul_(0.5).to(torch.bfloat16)
-    pk = torch.empty((x.shape[0], D // 2), dtype=torch.uint8, device="cuda")
-    sc = torch.empty((x.shape[0], D // 16), dtype=torch.uint8, device="cuda")
-    for _ in range(3):
-        kv_quant(x, pk, sc)
-    tm = EventTimer(torch)
-    for _ in range(10):
-        s = tm.start()
-        kv_quant(x, pk, sc)
-        tm.stop(s, "quant")
-    torch.cuda.synchronize()
-    ms = tm.totals()["quant"][0] / 10
-    qbytes = x.numel() * 2 + pk.numel() + sc.numel()
-    res["kv_quant_12_frames"] = {"ms": round(ms, 5), "bytes": qbytes, "gbs": round(qbytes / ms / 1e6, 1),
-                                 "frac_hbm": round(qbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
-    del x, pk, sc
-    # recache at the prompt-switch shape (12 held frames, 512 text tokens), 30 layers
+    return res
+
+
+def recache_row(torch, shape, Cache, inputs):
+    """The prompt-switch recache (12 held frames, 512 text tokens) of every layer of a
+    filled 30-layer cache: per layer block-causal self + cross + slot rewrite."""
+    H, D = shape.heads, shape.head_dim
     L = 30
     cr = Cache(L, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
                shape.window_frames)
@@ -668,16 +689,12 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     # visible pairs: group g of 4680 rows sees (g+1)*4680 keys; cross: 512 keys
     self_pairs = sum(4680 * (gg + 1) * 4680 for gg in range(4))
     fl = L * (self_pairs + rows * 512) * H * 4 * D
-    res["recache_30_layers"] = {"ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
-                                "frac_bf16_peak": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
-                                "query_tokens_per_s": round(L * rows / ms * 1e3, 1),
-                                "note": "per layer: block-causal self + cross (512 text keys) + slot rewrite"}
+    row = {"ms": round(ms, 3), "tflops": round(fl / ms / 1e9, 1),
+           "frac_bf16_peak": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "query_tokens_per_s": round(L * rows / ms * 1e3, 1),
+           "note": "per layer: block-causal self + cross (512 text keys) + slot rewrite"}
     del cr, big, txt, o, ox
-    pool = gen_inputs(torch, 8, n, H, D, 21, "cuda")
-    res["stack_fp4"] = stack_row(torch, shape, Cache, attn_flops, "fp4", pool)
-    res["interactive_composite"] = composite_row(torch, shape, Cache, attn_flops, pool)
-    res["gemm_bf16_ceiling"] = gemm_ceiling_row(torch)
-    return res
+    return row
 
 
 def layer_stream_row(torch, shape, Cache, attn_flops, inputs, passes=5):
@@ -747,6 +764,16 @@ def main():
     from windowed_attention_kv_amd import Cache, attn_flops, kv_quant, synth
 
     layer_shape = synth.CONFIGS["layer"]
+    if args.row:
+        torch.cuda.set_device(0)
+        ls = layer_shape
+        inputs = gen_inputs(torch, ls.chunks, ls.n_query, ls.heads, ls.head_dim, 7, "cuda")
+        if args.row == "share":
+            rows = share_rows(torch, ls, Cache, attn_flops, inputs)
+        else:
+            rows = {"recache_30_layers": recache_row(torch, ls, Cache, inputs)}
+        print(json.dumps({"row": args.row, "rows": rows}), flush=True)
+        return
     shape = synth.CONFIGS["stack"]
     L, steps, chunks = shape.layers, shape.steps, shape.chunks
     n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame

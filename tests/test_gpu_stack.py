@@ -1,5 +1,5 @@
-"""GPU parity of the multi-layer workloads: the FP4 store on the 30-layer stack, the
-prompt-switch recache of every layer of a 30-layer cache, and the batched commit
+"""GPU parity of the multi-layer workloads: the 30-layer stack at its full length (bf16
+and FP4 stores), the prompt-switch recache of every layer of a 30-layer cache, and the batched commit
 (ll_cache_commit_layers) against per-layer commits and the oracle."""
 import numpy as np
 import pytest
@@ -13,24 +13,37 @@ from windowed_attention_kv_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-class _PoolModel(LayerModel):
-    """LayerModel whose FP4 store runs fp4.quantize / dequantize once per distinct committed
-    frame buffer: the stack's resident input sets recur across layers and chunks, and the
-    codec is the oracle's cost. Storage is otherwise LayerModel's."""
+class _StreamModel(LayerModel):
+    """LayerModel for the full-length stack. Frames of the resident input sets are converted
+    (under FP4: encoded and decoded) once and shared by every layer and chunk that commits
+    them; a committed frame is dropped as soon as the layer no longer holds it, so 80 chunks
+    stay within a few hundred MB. keys_for_chunk still asserts that every committed frame a
+    chunk sees is held, so a dropped frame that a chunk needed fails loudly. The memo keeps a
+    reference to each source frame, so no key can be reused by another buffer."""
     memo = {}
 
     def _store(self, f, kv, bits, dst, dst_fp4):
-        if self.kv_format != "fp4":
-            return super()._store(f, kv, bits, dst, dst_fp4)
-        key = (bits.__array_interface__["data"][0], bits.shape)
+        src = bits if self.kv_format == "fp4" else kv
+        key = (self.kv_format, src.__array_interface__["data"][0], src.shape)
         if key not in self.memo:
-            rows = np.asarray(bits).reshape(self.T * self.H, self.D)
-            packed, scales = ofp4.quantize(rows)
-            self.memo[key] = (packed, scales,
-                              ofp4.dequantize(packed, scales).reshape(self.T, self.H, self.D))
-        packed, scales, values = self.memo[key]
-        dst_fp4[f] = (packed, scales)
+            if self.kv_format == "fp4":
+                rows = np.asarray(bits).reshape(self.T * self.H, self.D)
+                packed, scales = ofp4.quantize(rows)
+                values = ofp4.dequantize(packed, scales).reshape(self.T, self.H, self.D)
+                self.memo[key] = (src, (packed, scales), values)
+            else:
+                self.memo[key] = (src, None, np.asarray(kv, dtype=np.float64))
+        _, planes, values = self.memo[key]
+        if planes is not None:
+            dst_fp4[f] = planes
         dst[f] = values
+
+    def commit(self, k, v, k_bits=None, v_bits=None):
+        super().commit(k, v, k_bits, v_bits)
+        held = set(self.held())
+        for d in (self.k, self.v, self.k_fp4, self.v_fp4):
+            for f in [f for f in d if f not in held]:
+                del d[f]
 
 
 def _cache(shape, layers, kv_format="dense"):
@@ -44,72 +57,91 @@ def _model(shape, kv_format="dense", cls=LayerModel):
                shape.tokens_per_frame, shape.heads, shape.head_dim, kv_format=kv_format)
 
 
-def test_fp4_stack_config_sampled():
-    """The FP4 stack as the bench runs it: one 30-layer FP4 cache; per chunk 4 denoise steps
-    over all layers, then one batched commit of the last step's K/V into all 30 layers; 16
-    chunks (fill-up, the window's wrap, the sink retiring into its slots). Every call takes
-    seeded inputs: layers 0, 15 and 29 fresh ones at step 0 of chunks 0, 1, 4, 5 and 15, every
-    other call one of four resident sets. Those layers are checked against per-layer FP4
-    oracles on sampled rows at steps 0 and 3 of those chunks; at the end every layer's exported
-    codes and scales equal, bit for bit, the oracle's encoding of the K/V committed into each
-    slot."""
+@pytest.mark.parametrize("kv_format", ["dense", "fp4"])
+def test_stack_config_sampled(kv_format):
+    """The stack workload at its full length, as the bench runs it: one 30-layer cache (bf16
+    or FP4 store); per chunk 4 denoise steps over all layers, then one batched commit of the
+    last step's K/V into all 30 layers; 80 chunks (fill-up, the window's wrap, the sink
+    retiring into its slots, and 76 chunks of steady state). Layers 0, 15 and 29 are checked
+    against per-layer oracles on sampled rows at steps 0 and 3 of chunks 0, 1, 4, 5, 15, 39, 40
+    and 79: at step 0 they take fresh seeded inputs, every other call takes one of five
+    resident input sets, chosen so that consecutive chunks of a layer commit different sets.
+    At the end every layer's exported slots equal, bit for bit, the K/V committed into each
+    slot (under FP4: the oracle's encoding of it)."""
     import torch
     shape = synth.CONFIGS["layer"]
-    L, steps, n_chunks = 30, 4, 16
+    L, steps, n_chunks = 30, 4, 80
     C, S, W, T = shape.chunk_frames, shape.sink_frames, shape.window_frames, shape.tokens_per_frame
     n, H, D = shape.n_query, shape.heads, shape.head_dim
-    sampled_layers, sampled_chunks = (0, 15, 29), {0, 1, 4, 5, 15}
-    rows = sample_rows(n, 16, seed=11)
-    log("case: FP4 stack, 30 layers x 4 steps x 16 chunks, sampled layers/chunks/rows")
-    pool_host = [synth.chunk_inputs(shape, 100 + i, 0, 0) for i in range(4)]
+    fp4 = kv_format == "fp4"
+    sampled_layers, sampled_chunks = (0, 15, 29), {0, 1, 4, 5, 15, 39, 40, 79}
+    rows = sample_rows(n, 16, seed=11 if fp4 else 9)
+    log(f"case: {kv_format} stack, 30 layers x 4 steps x 80 chunks, sampled layers/chunks/rows")
+    pool_host = [synth.chunk_inputs(shape, 100 + i, 0, 0) for i in range(5)]
     pool = [tuple(t.torch("cuda") for t in trip) for trip in pool_host]
-    cache = _cache(shape, L, "fp4")
-    models = {l: _model(shape, "fp4", _PoolModel) for l in sampled_layers}
-    committed = {}          # (layer, chunk) -> pool index committed
+
+    def pick(c, st, layer):
+        return (c + 2 * st + layer) % len(pool)
+
+    cache = _cache(shape, L, kv_format)
+    models = {l: _model(shape, kv_format, _StreamModel) for l in sampled_layers}
+    committed = {}          # (layer, chunk) -> input set committed
     for c in range(n_chunks):
         for st in range(steps):
             for layer in range(L):
-                idx = (c * steps * L + st * L + layer) % len(pool)
-                fresh = layer in models and st == 0 and c in sampled_chunks
-                host = synth.chunk_inputs(shape, layer, st, c) if fresh else pool_host[idx]
-                dev = tuple(t.torch("cuda") for t in host) if fresh else pool[idx]
+                check = layer in models and c in sampled_chunks and st in (0, steps - 1)
+                fresh = check and st == 0
+                host = synth.chunk_inputs(shape, layer, st, c) if fresh else pool_host[pick(c, st, layer)]
+                dev = tuple(t.torch("cuda") for t in host) if fresh else pool[pick(c, st, layer)]
                 o = cache.attn_chunk(layer, *dev)
-                if layer in models and c in sampled_chunks and st in (0, steps - 1):
+                if check:
                     q, k, v = host
                     ref = models[layer].attn_chunk(q.values, k.values, v.values, rows=rows)
-                    assert_close(to_np(o)[rows], ref, "bf16", f"FP4 layer {layer} chunk {c} step {st}")
-                if st == steps - 1:
-                    committed[(layer, c)] = idx
-        last = [(c * steps * L + (steps - 1) * L + layer) % len(pool) for layer in range(L)]
+                    assert_close(to_np(o[torch.as_tensor(rows, device="cuda")]), ref, "bf16",
+                                 f"{kv_format} layer {layer} chunk {c} step {st}")
+        last = [pick(c, steps - 1, layer) for layer in range(L)]
         cache.commit_layers(0, [pool[i][1] for i in last], [pool[i][2] for i in last])
+        for layer in range(L):
+            committed[(layer, c)] = last[layer]
         for layer, m in models.items():
             _, k, v = pool_host[last[layer]]
             m.commit(k.values, v.values, k.bits, v.bits)
     torch.cuda.synchronize()
     F = n_chunks * C
     slot_frames = ring.slot_map(F, S, W)
-    want = {}               # (input set, frame of the chunk, K|V) -> oracle codes and scales
+    want = {}               # (input set, frame of the chunk, K|V) -> expected slot contents
 
-    def encoded(idx, i, which):
+    def expected(idx, i, which):
         if (idx, i, which) not in want:
-            src = pool_host[idx][1 + which].bits[i * T:(i + 1) * T].reshape(T * H, D)
-            want[(idx, i, which)] = ofp4.quantize(src)
+            src = pool_host[idx][1 + which]
+            if fp4:
+                want[(idx, i, which)] = ofp4.quantize(src.bits[i * T:(i + 1) * T].reshape(T * H, D))
+            else:
+                want[(idx, i, which)] = pool[idx][1 + which][i * T:(i + 1) * T]
         return want[(idx, i, which)]
 
     for layer in range(L):
-        kp, ks, vp, vs = (x.cpu().numpy() for x in cache.export(layer))
+        planes = cache.export(layer)
         Fs, slots = cache.state(layer)
         assert Fs == F and slots == slot_frames
+        if fp4:
+            kp, ks, vp, vs = (x.cpu().numpy() for x in planes)
         for slot, f in enumerate(slot_frames):
             idx, i = committed[(layer, f // C)], f % C
-            sl = slice(slot * T * H, (slot + 1) * T * H)
-            for got_p, got_s, which, name in ((kp, ks, 0, "K"), (vp, vs, 1, "V")):
-                wp, ws = encoded(idx, i, which)
-                assert np.array_equal(got_p[sl], wp), (layer, slot, f, name, "codes")
-                assert np.array_equal(got_s[sl], ws), (layer, slot, f, name, "scales")
-        if layer in models:
+            if fp4:
+                sl = slice(slot * T * H, (slot + 1) * T * H)
+                for got_p, got_s, which, name in ((kp, ks, 0, "K"), (vp, vs, 1, "V")):
+                    wp, ws = expected(idx, i, which)
+                    assert np.array_equal(got_p[sl], wp), (layer, slot, f, name, "codes")
+                    assert np.array_equal(got_s[sl], ws), (layer, slot, f, name, "scales")
+            else:
+                for got, which, name in ((planes[0], 0, "K"), (planes[1], 1, "V")):
+                    assert torch.equal(got[slot * T:(slot + 1) * T], expected(idx, i, which)), \
+                        (layer, slot, f, name)
+        if fp4 and layer in models:
             mkp, mks, mvp, mvs, valid = models[layer].export_fp4()
-            assert np.array_equal(kp[valid], mkp[valid]) and np.array_equal(vs[valid], mvs[valid])
+            for got, ref in ((kp, mkp), (ks, mks), (vp, mvp), (vs, mvs)):
+                assert np.array_equal(got[valid], ref[valid]), layer
 
 
 def test_recache_30_layers_sampled():
