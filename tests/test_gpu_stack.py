@@ -251,38 +251,57 @@ def test_commit_layers_equals_per_layer_commits(kv_format):
                         assert torch.equal(x[sl], y[sl]), (c, layer, slot, f)
 
 
-def test_commit_layers_against_the_oracle():
-    """Batched commits into 4 layers of a smaller FP4 and dense cache (T = 200, all 12 heads)
-    checked against the oracle's export after every batch, through the wrap and a shot."""
+_BATCHED_CASES = {
+    # name: (base config, overrides, kv_format)
+    "bf16-d128-dense": ("layer", dict(tokens_per_frame=200), "dense"),
+    "bf16-d128-fp4": ("layer", dict(tokens_per_frame=200), "fp4"),
+    "bf16-d64-dense": ("layer", dict(tokens_per_frame=96, heads=6, head_dim=64), "dense"),
+    "bf16-d64-fp4": ("layer", dict(tokens_per_frame=96, heads=6, head_dim=64), "fp4"),
+    "f32-d64": ("tiny", dict(), "dense"),
+}
+
+
+@pytest.mark.parametrize("case", list(_BATCHED_CASES))
+def test_commit_layers_against_the_oracle(case):
+    """Batched commits into 4 layers checked against the oracle's export after every batch,
+    through the window's wrap, the sink retiring into its slots and a new shot in one layer;
+    bf16 and FP4 stores at head_dim 128 and 64 (16-byte units of 16 and 8 per head row; one or
+    two 64-element FP4 groups) and an fp32 cache (the tiny shape). Afterwards one more chunk of
+    attention per layer reads the batched-committed cache."""
     import torch
-    for kv_format in ("dense", "fp4"):
-        shape = synth.shrink(synth.CONFIGS["layer"], name=f"batched-{kv_format}", tokens_per_frame=200)
-        L = 4
-        log(f"case: batched commit vs oracle, {kv_format}")
-        cache = _cache(shape, L, kv_format)
-        models = [_model(shape, kv_format) for _ in range(L)]
-        for c in range(7):
-            if c == 3:
-                cache.new_shot(2)
-                models[2].new_shot()
-            ins = [synth.chunk_inputs(shape, layer, 0, c, salt=3) for layer in range(L)]
-            cache.commit_layers(0, [x[1].torch("cuda") for x in ins], [x[2].torch("cuda") for x in ins])
-            for layer in range(L):
-                _, k, v = ins[layer]
-                models[layer].commit(k.values, v.values, k.bits, v.bits)
-            torch.cuda.synchronize()
-            for layer in range(L):
-                m = models[layer]
-                F, slots = cache.state(layer)
-                assert F == m.F and slots == m.slot_map()
-                if kv_format == "fp4":
-                    got = [x.cpu().numpy() for x in cache.export(layer)]
-                    want = m.export_fp4()
-                    valid = want[4]
-                    for gg, ww in zip(got, want[:4]):
-                        assert np.array_equal(gg[valid], ww[valid]), (c, layer)
-                else:
-                    K, V = (to_np(x) for x in cache.export(layer))
-                    MK, MV = m.export_dense()
-                    valid = ~np.isnan(MK[:, 0, 0])
-                    assert np.array_equal(K[valid], MK[valid]) and np.array_equal(V[valid], MV[valid])
+    base, over, kv_format = _BATCHED_CASES[case]
+    shape = synth.shrink(synth.CONFIGS[base], name=f"batched-{case}", **over)
+    L = 4
+    log(f"case: batched commit vs oracle, {case}")
+    cache = _cache(shape, L, kv_format)
+    models = [_model(shape, kv_format) for _ in range(L)]
+    for c in range(7):
+        if c == 3:
+            cache.new_shot(2)
+            models[2].new_shot()
+        ins = [synth.chunk_inputs(shape, layer, 0, c, salt=3) for layer in range(L)]
+        cache.commit_layers(0, [x[1].torch("cuda") for x in ins], [x[2].torch("cuda") for x in ins])
+        for layer in range(L):
+            _, k, v = ins[layer]
+            models[layer].commit(k.values, v.values, k.bits, v.bits)
+        torch.cuda.synchronize()
+        for layer in range(L):
+            m = models[layer]
+            F, slots = cache.state(layer)
+            assert F == m.F and slots == m.slot_map()
+            if kv_format == "fp4":
+                got = [x.cpu().numpy() for x in cache.export(layer)]
+                want = m.export_fp4()
+                valid = want[4]
+                for gg, ww in zip(got, want[:4]):
+                    assert np.array_equal(gg[valid], ww[valid]), (c, layer)
+            else:
+                K, V = (to_np(x) for x in cache.export(layer))
+                MK, MV = m.export_dense()
+                valid = ~np.isnan(MK[:, 0, 0])
+                assert np.array_equal(K[valid], MK[valid]) and np.array_equal(V[valid], MV[valid])
+    for layer in range(L):
+        q, k, v = synth.chunk_inputs(shape, layer, 0, 7, salt=4)
+        o = cache.attn_chunk(layer, q.torch("cuda"), k.torch("cuda"), v.torch("cuda"))
+        assert_close(to_np(o), models[layer].attn_chunk(q.values, k.values, v.values), shape.dtype,
+                     f"{case} layer {layer} chunk after the batched commits")
