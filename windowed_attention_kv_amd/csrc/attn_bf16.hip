@@ -534,6 +534,16 @@ __device__ __forceinline__ v4i16_t lds_read_tr(const uint8_t* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
 }
 
+// V^T operand i of the PV product (i = 4 db + 2 kb + j: head dims 32 db.., keys 32 kb + 16 j..)
+// from a key-major V sub-tile at vt: two transposing reads of 4 key rows each
+__device__ __forceinline__ bf16x8_t read_v_operand(const uint8_t* vt, const int (&vbase)[4], int i) {
+  const int db = i / 4, kb = (i / 2) & 1, j = i & 1;
+  const uint8_t* a0 = vt + vbase[db] + (kb * 32 + 16 * j) * DT_ROW;
+  const v4i16_t lo = lds_read_tr(a0);
+  const v4i16_t hi4 = lds_read_tr(a0 + 8 * DT_ROW);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
                                            voff, 0, 0, 0);
@@ -870,6 +880,16 @@ void attn_bf16_direct_kernel(Params p) {
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPipe, 0);
       }
+      // Dense tiles: the V operands of the first kPipe PV MFMAs are read right after the QK
+      // MFMAs, so they land during the softmax and the PV block starts on an MFMA instead of
+      // an LDS wait (16 more registers; the FP4 instantiation has none to spare).
+      constexpr bool kVEarly = !FP4;
+      bf16x8_t va_early[kPipe];
+      if constexpr (kVEarly) {
+#pragma unroll
+        for (int i = 0; i < kPipe; ++i) va_early[i] = read_v_operand(vt, vbase, i);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPipe, 0);
+      }
 
       // mask: rows past the segment's end, and keys past this row's block-causal limit
       if (seg_left < BN || key0 + BN > wave_min_lim) {
@@ -906,19 +926,13 @@ void attn_bf16_direct_kernel(Params p) {
         constexpr int NP = (D / 32) * 4;
         bf16x8_t va[NP];
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          const int db = i / 4, kb = (i / 2) & 1, j = i & 1;
-          const uint8_t* a0 = vt + vbase[db] + (kb * 32 + 16 * j) * DT_ROW;
-          const v4i16_t lo = lds_read_tr(a0);
-          const v4i16_t hi4 = lds_read_tr(a0 + 8 * DT_ROW);
-          va[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
+        for (int i = 0; i < NP; ++i) va[i] = kVEarly && i < kPipe ? va_early[i] : read_v_operand(vt, vbase, i);
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           const int db = i / 4, kb = (i / 2) & 1, j = i & 1;
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[kb][j], oacc[db], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPipe, 0);
+        if (!kVEarly) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPipe, 0);
 #pragma unroll
         for (int i = 0; i < NP - kPipe; ++i) {
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
