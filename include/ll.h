@@ -28,8 +28,10 @@
  * thread-safe. No call reads anything back from the device.
  *
  * Errors. Every call returns an ll_status. All validation happens before anything is
- * enqueued; on any error no metadata changes and nothing is enqueued (except LL_EDEVICE,
- * reported when a launch fails, in which case metadata also stays unchanged).
+ * enqueued; on any error no metadata changes and nothing is enqueued, except LL_EDEVICE
+ * (the HIP runtime refused a launch): metadata still stays unchanged, but cache contents that
+ * an earlier launch of the same call already wrote (a batched commit of more than 32 layers
+ * runs several launches) are then undefined, so reset the cache after LL_EDEVICE.
  * ll_last_error() gives a message for the last failing call on the calling thread.
  * No call aborts the process.
  */
@@ -147,8 +149,8 @@ ll_status ll_attn_chunk_noalloc(ll_cache* cache, int32_t layer, const void* q, c
  * with qx, ox: [C*T, H, D] and k_text, v_text: [n_text, H, D], n_text >= 1, in the cache's
  * dtype (the text K/V are never quantised). For a dense bf16 head_dim-128 cache both parts
  * run in one kernel launch (the cross blocks take the compute units the self-attention leaves
- * idle); otherwise (FP4 store, head_dim 64, fp32) as two launches on `stream`. Errors as ll_attn_chunk, plus LL_EINVAL for a
- * NULL text pointer or an n_text out of range. */
+ * idle); otherwise (FP4 store, head_dim 64, fp32) as two launches on `stream`. Errors as
+ * ll_attn_chunk, plus LL_EINVAL for a NULL text pointer or an n_text out of range. */
 ll_status ll_attn_chunk_cross(ll_cache* cache, int32_t layer, const void* q, const void* k,
                               const void* v, const void* qx, const void* k_text,
                               const void* v_text, int32_t n_text, void* o, void* ox,
@@ -168,9 +170,9 @@ ll_status ll_cache_commit(ll_cache* cache, int32_t layer, const void* k, const v
  * pointers; k and v are HOST arrays of n_layers pointers, read during the call only). Each
  * layer gets exactly what ll_cache_commit would give it (its own frame count and shot), so
  * layers may be at different frames. Committing every layer of a denoise step at once moves
- * enough bytes per launch to run the commit at full HBM bandwidth ("为什么视频生成是一个基础设施
- * 问题", §3 and §4: KV-cache update and movement become visible costs once the denoise steps
- * are few). Every layer is validated before anything is enqueued; on any error no layer's
+ * 30x a single layer's bytes per launch, which a one-layer launch is too small to stream at
+ * the device's copy rate ("为什么视频生成是一个基础设施问题", §3 and §4: KV-cache update and
+ * movement become visible costs once the denoise steps are few). Every layer is validated before anything is enqueued; on any error no layer's
  * metadata changes. LL_EINVAL for a bad handle, layer range, or a NULL / misaligned pointer. */
 ll_status ll_cache_commit_layers(ll_cache* cache, int32_t first_layer, int32_t n_layers,
                                  const void* const* k, const void* const* v, void* stream);
