@@ -1,5 +1,6 @@
-"""Build the HIP library (libll.so, gfx950), the CPU-only recording variant (libll_fake.so)
-and its sanitizer-instrumented twin (libll_fake_san.so) in-tree. Run `python -m windowed_attention_kv_amd.build`."""
+"""Build the HIP library (libll.so, gfx950), the CPU-only recording variant (libll_fake.so),
+its sanitizer-instrumented twin (libll_fake_san.so) and the plain-C consumer the C-ABI test
+runs (tests/c_abi_stream) in-tree. Run `python -m windowed_attention_kv_amd.build`."""
 from __future__ import annotations
 
 import os
@@ -16,6 +17,9 @@ HOST_SOURCES = ["ll_host.cpp"]
 LIB = os.path.join(PKG, "libll.so")
 FAKE_LIB = os.path.join(PKG, "libll_fake.so")
 SAN_LIB = os.path.join(PKG, "libll_fake_san.so")
+C_CONSUMER_SRC = os.path.join(ROOT, "tests", "c_abi_stream.c")
+C_CONSUMER = os.path.join(ROOT, "tests", "c_abi_stream")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed-fp32 VALU ops are disabled for every HIP object (hipcc emits them on its own from
@@ -67,6 +71,14 @@ def build(verbose: bool = False) -> None:
     host_sources = [os.path.join(CSRC, "ll_host.cpp"), os.path.join(CSRC, "fake_launch.cpp")]
     _run(["g++", *HOST_FLAGS, *SAN_FLAGS, "-shared", *host_sources, "-o", tmp])
     shutil.move(tmp, SAN_LIB)
+    # a plain-C program against include/ll.h and libll.so (host code only: gcc, HIP runtime API)
+    tmp = C_CONSUMER + ".tmp"
+    _run(["gcc", "-std=c11", "-O1", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+          "-I", os.path.join(ROCM, "include"), "-D__HIP_PLATFORM_AMD__", C_CONSUMER_SRC,
+          "-L", PKG, "-lll", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN/../windowed_attention_kv_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib"),
+          "-o", tmp])
+    shutil.move(tmp, C_CONSUMER)
 
 
 if __name__ == "__main__":
