@@ -18,6 +18,7 @@ workloads, each timed on its own after the main loop.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -28,6 +29,41 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 (published)
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E (published)
+
+
+# hipDeviceAttribute_t values of the ROCm 7 HIP runtime (hip_runtime_api.h); they are only
+# trusted when the multiprocessor count read this way equals torch's
+HIP_ATTR_CLOCK_KHZ, HIP_ATTR_LDS_PER_CU, HIP_ATTR_MEM_CLOCK_KHZ = 5, 10002, 60
+HIP_ATTR_MEM_BUS_BITS, HIP_ATTR_CUS = 59, 63
+
+
+def device_info(torch):
+    """The device the peaks above are meant for, as the runtime reports it: name, architecture,
+    compute units, L2 and HBM sizes (torch), peak shader clock, LDS per CU and memory clock and
+    bus width (HIP attributes, through the runtime torch already loaded), and the bf16 dense
+    MFMA peak they imply (4096 bf16 flop per clock per CU). The HBM peak stays the published
+    8 TB/s: the transfers per reported memory clock depend on the memory type."""
+    prop = torch.cuda.get_device_properties(0)
+    info = {"name": prop.name, "arch": prop.gcnArchName, "compute_units": prop.multi_processor_count,
+            "l2_bytes_per_xcd": prop.L2_cache_size, "hbm_bytes": prop.total_memory}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+    except OSError:
+        return info
+
+    def attr(code):
+        v = ctypes.c_int(0)
+        return v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(code), ctypes.c_int(0)) == 0 else None
+
+    if attr(HIP_ATTR_CUS) != prop.multi_processor_count:
+        return info
+    clk, lds = attr(HIP_ATTR_CLOCK_KHZ), attr(HIP_ATTR_LDS_PER_CU)
+    mclk, bus = attr(HIP_ATTR_MEM_CLOCK_KHZ), attr(HIP_ATTR_MEM_BUS_BITS)
+    info.update({"peak_clock_ghz": clk / 1e6 if clk else None, "lds_bytes_per_cu": lds,
+                 "mem_clock_ghz": mclk / 1e6 if mclk else None, "mem_bus_bits": bus})
+    if clk:
+        info["bf16_dense_peak_tflops_from_clock"] = round(prop.multi_processor_count * 4096 * clk * 1e3 / 1e12, 1)
+    return info
 
 
 def parse():
@@ -841,6 +877,7 @@ def main():
                      "kernel": "attn_bf16_direct_kernel<8,2,false,false>",
                      "avg_launch_ms": round(attn_ms, 4),
                      "avg_flops_per_launch": attn_flops_launch},
+        "device": device_info(torch),
         "rows": {"commit_layers_in_stack": {
             "avg_launch_ms": round(commit_ms, 4), "layers_per_launch": L, "bytes": commit_bytes,
             "us_per_layer": round(commit_ms * 1e3 / L, 3),
