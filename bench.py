@@ -73,9 +73,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the FP4 / recache rows")
-    ap.add_argument("--row", choices=["share", "recache"], default=None,
+    ap.add_argument("--row", choices=["share", "recache", "vendor-flash"], default=None,
                     help="run only this workload (for profiling) and print its row: the 3-head "
-                         "share streams or the 30-layer recache")
+                         "share streams, the 30-layer recache or the vendor flash attention "
+                         "on the steady chunk's shape")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -659,6 +660,7 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     res["stack_fp4"] = stack_row(torch, shape, Cache, attn_flops, "fp4", pool)
     res["interactive_composite"] = composite_row(torch, shape, Cache, attn_flops, pool)
     res["gemm_bf16_ceiling"] = gemm_ceiling_row(torch)
+    res["vendor_flash_attention_same_shape"] = sdpa_context_row(torch, shape, attn_flops)
     return res
 
 
@@ -786,6 +788,56 @@ def gemm_ceiling_row(torch, m=8192):
             "note": f"torch.matmul bf16 {m}x{m}x{m}: the vendor GEMM's sustained rate on this device"}
 
 
+def sdpa_context_row(torch, shape, attn_flops):
+    """Context for the attention roofline: torch's fused attention (scaled_dot_product_attention
+    restricted to its flash backend, so it can never fall back to the unfused path) on the
+    steady chunk's shape: 4680 queries x 23400 keys x 12 heads x 128, bf16, no mask. Timed with
+    each flash library the torch build offers (AOTriton, CK); a library it lacks is reported as
+    unavailable."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    n, H, D = shape.n_query, shape.heads, shape.head_dim
+    keys = (shape.sink_frames + shape.window_frames + shape.chunk_frames) * shape.tokens_per_frame
+    g = torch.Generator(device="cuda")
+    g.manual_seed(23)
+    q = (torch.randn((1, H, n, D), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    k = (torch.randn((1, H, keys, D), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    v = (torch.randn((1, H, keys, D), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    flops = attn_flops(n, keys, H, D)
+    res = {"keys": keys,
+           "note": "torch.nn.functional.scaled_dot_product_attention, flash backend only, same shape "
+                   "as the steady chunk call"}
+    pick = getattr(torch.backends.cuda, "preferred_rocm_fa_library", None)
+    before = pick() if pick else None
+    for lib in ("aotriton", "ck"):
+        try:
+            if pick:
+                pick(lib)
+            elif lib != "aotriton":
+                raise RuntimeError("this torch build has no flash-library switch")
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                for _ in range(3):
+                    o = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                reps = 10
+                e0.record()
+                for _ in range(reps):
+                    o = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+                e1.record()
+                torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            res[lib] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                        "frac_bf16_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+            del o
+        except RuntimeError as e:
+            res[lib] = {"unavailable": str(e).splitlines()[0][:200]}
+    if pick and before is not None:
+        pick(before)
+    del q, k, v
+    return res
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -806,6 +858,8 @@ def main():
         inputs = gen_inputs(torch, ls.chunks, ls.n_query, ls.heads, ls.head_dim, 7, "cuda")
         if args.row == "share":
             rows = share_rows(torch, ls, Cache, attn_flops, inputs)
+        elif args.row == "vendor-flash":
+            rows = {"vendor_flash_attention_same_shape": sdpa_context_row(torch, ls, attn_flops)}
         else:
             rows = {"recache_30_layers": recache_row(torch, ls, Cache, inputs)}
         print(json.dumps({"row": args.row, "rows": rows}), flush=True)
