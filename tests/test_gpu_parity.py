@@ -307,6 +307,11 @@ def test_kv_quant_rejects_wrong_outputs():
         with pytest.raises(ValueError):
             kv_quant(t, p, s)
     assert all(int(b) == 0 for b in kv_quant(t, good_p, good_s)[0].flatten()[:4])
+    # an output that starts off the 8-byte grid the kernel stores on is refused by the library
+    from windowed_attention_kv_amd import LLError
+    flat = torch.empty(8 * 16 + 4, dtype=torch.uint8, device="cuda")
+    with pytest.raises(LLError):
+        kv_quant(t, flat[4:].view(8, 16), good_s)
 
 
 def test_fp4_stream():
