@@ -126,12 +126,13 @@ __device__ __forceinline__ int32_t spill_slot(const ScatterP& p, int32_t r) {
 // consecutive token rows of ONE head and one plane (K or V), and the workgroups of a row span
 // enumerate the heads fastest, so the heads of a span run side by side and together read the
 // span's source rows whole while each writes one contiguous run of its head's slot. One
-// 16-byte source load per thread, non-temporal loads and stores (the data is touched once).
-// Against a row-major mapping (each thread one unit of several token rows of all heads, plain
-// accesses), at the layer shape with cold sources (one GPU, same box): the 30-layer dense batch
-// 73% of 8 TB/s instead of 65%, the FP4 batch 62-64% instead of 61%, single-layer commits 57%
-// instead of 54% (dense) and 48% instead of 43% (FP4); a commit that also moves three sink
-// frames, 55% instead of 59%.
+// 16-byte source load per thread and row (an FP4 lane takes two rows), non-temporal loads and
+// stores (the data is touched once). Against a row-major mapping (each thread one unit of
+// several token rows of all heads, plain accesses), at the layer shape with cold sources (one
+// GPU, same box): the 30-layer dense batch 73% of 8 TB/s instead of 65%, the FP4 batch 69-70%
+// instead of 61%, single-layer commits 57% instead of 54% (dense) and 47% instead of 43% (FP4);
+// a commit that also moves three sink frames, 55% instead of 59%. (Dense threads taking two or
+// four rows: 70% and 68%.)
 
 // Every kernel below issues its source load first and computes the destination while it is in
 // flight; the helpers take the loaded value.
@@ -192,6 +193,11 @@ __device__ __forceinline__ void commit_lane_fp4(uint4 x, uint8_t* pk, uint8_t* s
   }
 }
 
+// FP4 rows per lane: a lane's waves spend part of their life quantising and exchanging with no
+// load in flight, so each lane loads two rows before working on either (70% of 8 TB/s on the
+// 30-layer batch in a timing harness against 65% with one, 68% with four)
+constexpr int kFp4Units = 2;
+
 // Single-layer commit and recache rewrite: grid (H x row spans, K|V), rows p.row0.. of this
 // launch; each source frame rank goes to slot_of_rank (lead ranks to sink slots, the rest to
 // the window ring), and a rank in the spill range first moves the sink frame it overwrites.
@@ -213,25 +219,37 @@ __global__ __launch_bounds__(256) void scatter_dense_kernel(ScatterP p, int32_t 
                     spill >= 0 ? head + (int64_t(spill) * p.T + t) * row_bytes : nullptr);
 }
 
-// fp4: D / 8 lanes per head row (lpr_log2 = 3 or 4), 256 / that rows per workgroup
+// fp4: D / 8 lanes per head row (lpr_log2 = 3 or 4); each lane takes kFp4Units rows, 256 / (D / 8)
+// apart, loading all of them before quantising any, so a workgroup covers kFp4Units * 256 /
+// (D / 8) rows
 __global__ __launch_bounds__(256) void scatter_fp4_kernel(ScatterP p, int32_t nrows, int32_t lpr_log2) {
   const int which = blockIdx.y;
   const int32_t h = int32_t(blockIdx.x) % p.H;
   const int32_t span = int32_t(blockIdx.x) / p.H;
   const int32_t c = threadIdx.x & ((1 << lpr_log2) - 1);
-  const int32_t lr = span * (256 >> lpr_log2) + int32_t(threadIdx.x >> lpr_log2);
-  const bool live = lr < nrows;
-  const int32_t tr = p.row0 + (live ? lr : nrows - 1);   // rows past the end still join the exchanges
+  const int32_t rpw = 256 >> lpr_log2;
   const int32_t D = 8 << lpr_log2;
-  const uint4 x = load_nt(p.src[which] + (int64_t(tr) * p.H + h) * (D * 2) + c * 16);
-  const int32_t r = tr / p.T, t = tr - r * p.T;
+  uint4 x[kFp4Units];
+  int32_t tr[kFp4Units];
+  bool live[kFp4Units];
+#pragma unroll
+  for (int k = 0; k < kFp4Units; ++k) {
+    const int32_t lr = (span * kFp4Units + k) * rpw + int32_t(threadIdx.x >> lpr_log2);
+    live[k] = lr < nrows;
+    tr[k] = p.row0 + (live[k] ? lr : nrows - 1);   // rows past the end still join the exchanges
+    x[k] = load_nt(p.src[which] + (int64_t(tr[k]) * p.H + h) * (D * 2) + c * 16);
+  }
   const int64_t head_rows = int64_t(p.slots) * p.T;
-  const int64_t row = h * head_rows + int64_t(slot_of_rank(p, r)) * p.T + t;
-  const int32_t spill = spill_slot(p, r);
-  const int64_t mrow = h * head_rows + int64_t(spill) * p.T + t;
-  commit_lane_fp4(x, p.dst[which] + row * (D / 2), p.dst_scales[which] + row * (D / 16),
-                  spill >= 0 ? p.dst[which] + mrow * (D / 2) : nullptr,
-                  spill >= 0 ? p.dst_scales[which] + mrow * (D / 16) : nullptr, c, lpr_log2, live);
+#pragma unroll
+  for (int k = 0; k < kFp4Units; ++k) {
+    const int32_t r = tr[k] / p.T, t = tr[k] - r * p.T;
+    const int64_t row = h * head_rows + int64_t(slot_of_rank(p, r)) * p.T + t;
+    const int32_t spill = spill_slot(p, r);
+    const int64_t mrow = h * head_rows + int64_t(spill) * p.T + t;
+    commit_lane_fp4(x[k], p.dst[which] + row * (D / 2), p.dst_scales[which] + row * (D / 16),
+                    spill >= 0 ? p.dst[which] + mrow * (D / 2) : nullptr,
+                    spill >= 0 ? p.dst_scales[which] + mrow * (D / 16) : nullptr, c, lpr_log2, live[k]);
+  }
 }
 
 // ---- batched commit: one chunk into many layers per launch ----
@@ -278,29 +296,39 @@ __global__ __launch_bounds__(256) void commit_layers_dense_kernel(CommitLayersP 
                     r >= lo && r < hi ? head + (int64_t(s0 + (r - lo)) * p.T + t) * row_bytes : nullptr);
 }
 
-// fp4: D / 8 lanes per head row (lpr_log2 = 3 or 4), 256 / that rows per workgroup
+// fp4: D / 8 lanes per head row (lpr_log2 = 3 or 4), kFp4Units rows per lane as above
 __global__ __launch_bounds__(256) void commit_layers_fp4_kernel(CommitLayersP p, int32_t lpr_log2) {
   const int which = blockIdx.y & 1;
   const int layer = blockIdx.y >> 1;
   const int32_t h = int32_t(blockIdx.x) % p.H;
   const int32_t span = int32_t(blockIdx.x) / p.H;
   const int32_t c = threadIdx.x & ((1 << lpr_log2) - 1);
-  const int32_t tr_own = span * (256 >> lpr_log2) + int32_t(threadIdx.x >> lpr_log2);
-  const bool live = tr_own < p.n_rows;
-  const int32_t tr = live ? tr_own : p.n_rows - 1;   // rows past the end still join the exchanges
-  const int32_t lo = p.l[layer].spill_lo, hi = p.l[layer].spill_hi, s0 = p.l[layer].spill_slot0;
+  const int32_t rpw = 256 >> lpr_log2;
   const int32_t D = 8 << lpr_log2;
-  const uint4 x = load_nt(p.l[layer].src[which] + (int64_t(tr) * p.H + h) * (D * 2) + c * 16);
-  const int32_t r = tr / p.T, t = tr - r * p.T;
+  uint4 x[kFp4Units];
+  int32_t tr[kFp4Units];
+  bool live[kFp4Units];
+#pragma unroll
+  for (int k = 0; k < kFp4Units; ++k) {
+    const int32_t t0 = (span * kFp4Units + k) * rpw + int32_t(threadIdx.x >> lpr_log2);
+    live[k] = t0 < p.n_rows;
+    tr[k] = live[k] ? t0 : p.n_rows - 1;   // rows past the end still join the exchanges
+    x[k] = load_nt(p.l[layer].src[which] + (int64_t(tr[k]) * p.H + h) * (D * 2) + c * 16);
+  }
+  const int32_t lo = p.l[layer].spill_lo, hi = p.l[layer].spill_hi, s0 = p.l[layer].spill_slot0;
   const int64_t head_rows = int64_t(p.slots) * p.T;
-  const int64_t row = h * head_rows + int64_t(commit_slot(p.l[layer].ring0, r, p.W)) * p.T + t;
-  const bool move = r >= lo && r < hi;
-  const int64_t mrow = h * head_rows + int64_t(s0 + (r - lo)) * p.T + t;
   uint8_t* const dst = p.l[layer].dst[which];
   uint8_t* const dsc = p.l[layer].dst_scales[which];
-  commit_lane_fp4(x, dst + row * (D / 2), dsc + row * (D / 16),
-                  move ? dst + mrow * (D / 2) : nullptr, move ? dsc + mrow * (D / 16) : nullptr,
-                  c, lpr_log2, live);
+#pragma unroll
+  for (int k = 0; k < kFp4Units; ++k) {
+    const int32_t r = tr[k] / p.T, t = tr[k] - r * p.T;
+    const int64_t row = h * head_rows + int64_t(commit_slot(p.l[layer].ring0, r, p.W)) * p.T + t;
+    const bool move = r >= lo && r < hi;
+    const int64_t mrow = h * head_rows + int64_t(s0 + (r - lo)) * p.T + t;
+    commit_lane_fp4(x[k], dst + row * (D / 2), dsc + row * (D / 16),
+                    move ? dst + mrow * (D / 2) : nullptr, move ? dsc + mrow * (D / 16) : nullptr,
+                    c, lpr_log2, live[k]);
+  }
 }
 
 // standalone codec: one thread per 64 elements when the row length allows, else per 16
@@ -415,7 +443,7 @@ int launch_scatter(const ScatterArgs& a, void* stream, char* err) {
   }
   const int32_t uph = a.D * p.es / 16;             // 8, 16 or 32
   const int32_t lg = a.fp4 ? (a.D == 64 ? 3 : 4) : (uph == 8 ? 3 : (uph == 16 ? 4 : 5));
-  const int32_t rows_per_wg = 256 >> lg;
+  const int32_t rows_per_wg = (256 >> lg) * (a.fp4 ? kFp4Units : 1);
   // one launch covers at most 2^24 token rows (frame ranks stay far below the float-reciprocal
   // division's 2^24 limit)
   constexpr int32_t kRowsPerLaunch = 1 << 24;
@@ -465,7 +493,8 @@ int launch_commit_layers(const CommitLayersArgs& a, void* stream, char* err) {
     if (a.fp4) {
       // lanes per head row: D / 8 (8 or 16)
       const int32_t lpr_log2 = a.D == 64 ? 3 : 4;
-      const int32_t spans = (n_rows + (256 >> lpr_log2) - 1) / (256 >> lpr_log2);
+      const int32_t rows_per_wg = (256 >> lpr_log2) * kFp4Units;
+      const int32_t spans = (n_rows + rows_per_wg - 1) / rows_per_wg;
       p.units = a.H * (a.D / 64);
       hipLaunchKernelGGL(commit_layers_fp4_kernel, dim3(spans * a.H, 2 * nl), dim3(256), 0, s, p, lpr_log2);
     } else {
