@@ -196,7 +196,7 @@ ll_status ll_recache(ll_cache* cache, int32_t layer, const void* q, const void* 
  * packed [rows, row_len/2] bytes and scales [rows, row_len/16] e8m0 bytes. Per block of 16:
  * scale byte = max(exponent_field(max|x|) - 2, 0); codes = |x| * 2^-(scale-127) rounded to
  * {0,.5,1,1.5,2,3,4,6}, ties to the even code, saturating at 6; sign bit copied. Inputs
- * must be finite. Bit-exact and deterministic. x must be 16-byte aligned, packed 16-byte
+ * must be finite. Bit-exact and deterministic. x must be 16-byte aligned, packed 4-byte
  * aligned (8-byte when row_len % 64 != 0) and scales 4-byte aligned when row_len % 64 == 0;
  * LL_EINVAL for a NULL or misaligned pointer, rows < 0 or a row_len that is not a positive
  * multiple of 16 (rows == 0 is a no-op). */

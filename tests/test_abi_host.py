@@ -385,15 +385,16 @@ def test_kv_quant_validation(fake):
     assert fake.ll_kv_quant(P, -1, 16, P, P, None) == _lib.LL_EINVAL
     assert fake.ll_kv_quant(P, 0, 16, P, P, None) == 0
     assert fake.ll_kv_quant(P, 3, 32, None, P, None) == _lib.LL_EINVAL
-    # output alignment the kernels store with: packed 16 (64-element groups) or 8, scales 4
+    # output alignment the kernels store with: packed 4 (64-element groups: one code word per
+    # 8 elements) or 8, scales 4
     fake.llfake_reset()
-    assert fake.ll_kv_quant(P, 3, 64, _at(8), P, None) == _lib.LL_EINVAL
+    assert fake.ll_kv_quant(P, 3, 64, _at(2), P, None) == _lib.LL_EINVAL
     assert fake.ll_kv_quant(P, 3, 64, P, _at(2), None) == _lib.LL_EINVAL
     assert fake.ll_kv_quant(_at(8), 3, 64, P, P, None) == _lib.LL_EINVAL
     assert fake.ll_kv_quant(P, 3, 32, _at(4), P, None) == _lib.LL_EINVAL
     assert fake.llfake_count() == 0
     assert fake.ll_kv_quant(P, 3, 32, _at(8), _at(1), None) == 0
-    assert fake.ll_kv_quant(P, 3, 64, _at(16), _at(4), None) == 0
+    assert fake.ll_kv_quant(P, 3, 64, _at(4), _at(4), None) == 0
     fake.llfake_reset()
     assert fake.ll_kv_quant(P, 3, 32, P, P, None) == 0
     assert _records(fake)[0][0] == 2

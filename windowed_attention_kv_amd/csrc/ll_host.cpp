@@ -551,11 +551,11 @@ ll_status ll_kv_quant(const void* x_bf16, int64_t rows, int32_t row_len, uint8_t
   if (rows == 0) return ok();
   if (ll_status s = check_ptr(x_bf16, "x")) return s;
   if (!packed || !scales) return fail(LL_EINVAL, "packed/scales is NULL");
-  // the kernels store 64 elements' codes as two 16-byte words and their 4 scale bytes as one
+  // the kernels store 8 elements' codes as one 4-byte word and 64 elements' scale bytes as one
   // word (row_len % 64 == 0), else 16 elements' codes as one 8-byte word and single scale bytes
   const bool g64 = row_len % 64 == 0;
-  if (!aligned(packed, g64 ? 16 : 8))
-    return fail(LL_EINVAL, "packed is not %d-byte aligned", g64 ? 16 : 8);
+  if (!aligned(packed, g64 ? 4 : 8))
+    return fail(LL_EINVAL, "packed is not %d-byte aligned", g64 ? 4 : 8);
   if (g64 && !aligned(scales, 4)) return fail(LL_EINVAL, "scales is not 4-byte aligned");
   if (rows > (int64_t(1) << 40) / row_len) return fail(LL_EINVAL, "input too large");
   ll::QuantArgs a;
