@@ -29,6 +29,9 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 (published)
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E (published)
+# GPU spin ahead of each timed batch of the cache and codec rows (gpu_hold): longer than the
+# host needs to enqueue a batch (30 Python-level commit calls)
+HOLD_MS = 3.0
 
 
 # hipDeviceAttribute_t values of the ROCm 7 HIP runtime (hip_runtime_api.h); they are only
@@ -146,6 +149,36 @@ def gen_inputs(torch, n_chunks, n, H, D, seed, device):
     return out
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def gpu_hold(torch, ms):
+    """Enqueue a GPU spin of about `ms` milliseconds (torch's sleep kernel, its cycle count
+    calibrated once with events). A start event recorded after it fires only when the spin
+    ends, by which time the host has enqueued the timed calls: the events then measure the
+    GPU's own time for back-to-back launches, not the host's argument marshalling between
+    them. Returns False (and enqueues nothing) if the spin cannot be calibrated."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        _SLEEP_CYCLES_PER_MS = 0.0
+        try:
+            torch.cuda._sleep(1 << 20)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            torch.cuda._sleep(1 << 24)
+            b.record()
+            b.synchronize()
+            el = a.elapsed_time(b)
+            if el > 0.05:
+                _SLEEP_CYCLES_PER_MS = (1 << 24) / el
+        except (AttributeError, RuntimeError):
+            pass
+    if _SLEEP_CYCLES_PER_MS <= 0:
+        return False
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+    return True
+
+
 class EventTimer:
     """Pairs of HIP events recorded on the current (launch) stream."""
 
@@ -153,7 +186,10 @@ class EventTimer:
         self.torch = torch
         self.pairs = []
 
-    def start(self):
+    def start(self, hold_ms=0.0):
+        """Record a start event; with hold_ms, behind a GPU spin of that length (gpu_hold)."""
+        if hold_ms > 0:
+            gpu_hold(self.torch, hold_ms)
         e = self.torch.cuda.Event(enable_timing=True)
         e.record()
         return e
@@ -444,7 +480,8 @@ def commit_batch_row(torch, shape, Cache, kv_format, pairs, batched=False):
     """Per-layer commit time of 30 steady commits (one per layer of a 30-layer cache), either
     30 back-to-back ll_cache_commit calls or one ll_cache_commit_layers call for all 30
     layers (the stack workload's pattern). Every layer commits its own K/V pair (30 distinct
-    pairs, 862 MB: more than the caches hold, as in the stack); events bracket each batch."""
+    pairs, 862 MB: more than the caches hold, as in the stack); events bracket each batch,
+    recorded behind a GPU spin that covers the host's enqueueing of the batch (gpu_hold)."""
     L = 30
     n, H, D = shape.n_query, shape.heads, shape.head_dim
     cache = Cache(L, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
@@ -457,7 +494,7 @@ def commit_batch_row(torch, shape, Cache, kv_format, pairs, batched=False):
             cache.commit(layer, ks[layer], vs[layer])
     tm = EventTimer(torch)
     for rep in range(10):
-        s = tm.start()
+        s = tm.start(HOLD_MS)
         if batched:
             cache.commit_layers(0, ks, vs)
         else:
@@ -478,14 +515,15 @@ def commit_batch_row(torch, shape, Cache, kv_format, pairs, batched=False):
 def copy_ceiling_row(torch, pairs):
     """Context for the commit rows: a plain device copy (torch's copy kernel) of the bytes the
     batched commit moves: 30 distinct K/V pairs (2 x 14.38 MB each) copied back to back into
-    30 destination pairs; per-pair time, events bracketing each batch of 30."""
+    30 destination pairs; per-pair time, events bracketing each batch of 30 (behind a GPU spin,
+    as in commit_batch_row)."""
     dst = [(torch.empty_like(k), torch.empty_like(v)) for k, v in pairs]
     for (k, v), (dk, dv) in zip(pairs, dst):
         dk.copy_(k)
         dv.copy_(v)
     tm = EventTimer(torch)
     for rep in range(10):
-        s = tm.start()
+        s = tm.start(HOLD_MS)
         for (k, v), (dk, dv) in zip(pairs, dst):
             dk.copy_(k)
             dv.copy_(v)
@@ -519,7 +557,7 @@ def quant_chunk_row(torch, k, v):
         _lib.check(lib, lib.ll_kv_quant(*a))
     tm = EventTimer(torch)
     for rep in range(10):
-        s = tm.start()
+        s = tm.start(HOLD_MS)
         for a in args:
             lib.ll_kv_quant(*a)
         tm.stop(s, "batch")
@@ -537,7 +575,8 @@ def spill_commit_row(torch, shape, Cache, k, v):
     """The commit that retires a shot's sink frames from the window (multi-shot sink): with
     S = C = 3 and W = 9, the fourth commit after a shot boundary also moves the shot's first 3
     frames from their window slots to the sink slots. Per-commit time of 30 such commits (one
-    per layer); bytes = the plain commit's plus the moved frames read and written."""
+    per layer), events behind a GPU spin as in commit_batch_row; bytes = the plain commit's
+    plus the moved frames read and written."""
     L = 30
     n, H, D, T = shape.n_query, shape.heads, shape.head_dim, shape.tokens_per_frame
     C, S, W = shape.chunk_frames, shape.sink_frames, shape.window_frames
@@ -548,7 +587,7 @@ def spill_commit_row(torch, shape, Cache, k, v):
             cache.new_shot(layer)
             for _ in range(W // C):
                 cache.commit(layer, k, v)
-        s = tm.start()
+        s = tm.start(HOLD_MS)
         for layer in range(L):
             cache.commit(layer, k, v)
         tm.stop(s, "spill" if rep else "warm")
@@ -646,7 +685,7 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
         kv_quant(x, pk, sc)
     tm = EventTimer(torch)
     for _ in range(10):
-        s = tm.start()
+        s = tm.start(HOLD_MS)
         kv_quant(x, pk, sc)
         tm.stop(s, "quant")
     torch.cuda.synchronize()
