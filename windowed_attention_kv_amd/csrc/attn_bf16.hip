@@ -49,6 +49,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef float v4f32_t __attribute__((ext_vector_type(4)));
+typedef float v2f32_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u32_t __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 64;          // keys per tile
 constexpr float kLazyBound = 256.0f;   // largest allowed sum of a lane's weights in a tile
@@ -512,6 +516,9 @@ constexpr int DT_ROW = 256;                 // bytes per key row (128 bf16)
 // the AMDGPU backend (MFMA, LDS read)
 constexpr int kPipe = 4;
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+// cache-policy bits of a buffer access for the agent-scope (sc1) policy: the encoding an
+// agent-scope atomic load or store of one word gets
+constexpr int kSc1 = 16;
 // s_waitcnt immediate for vmcnt <= 4 with expcnt and lgkmcnt at 0 (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8)
 constexpr int kWaitVm4 = 0x0004;
@@ -559,10 +566,14 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* ld
 // block's counter; the one that sees the count complete merges the slots (main piece
 // first, then the tail pieces in range order) and stores O. No workgroup ever waits on
 // another.
+// A piece's state in its workspace slot: thread t's 64 O values as 16 groups of 4 (group g at
+// byte (g * threads + t) * 16), then its running max and sum as one 8-byte pair (at byte
+// 16 * 16 * threads + 8 t), so both publishing and merging move 16-byte and 8-byte words.
 template <int NW>
 struct SplitState {
   static constexpr int REGS = 66;               // 64 O values, running max, running sum
   static constexpr int SLOT_FLOATS = REGS * NW * 64;
+  static constexpr int ML_OFFSET = 16 * 16 * NW * 64;   // bytes before the (max, sum) pairs
   static_assert(NW != 8 || SLOT_FLOATS * 4 == kSplitSlotBytes, "slot size");
 };
 
@@ -975,15 +986,21 @@ void attn_bf16_direct_kernel(Params p) {
         __syncthreads();   // s_last is written again below
       }
       if (!from_regs) {
-        float* sp = p.part + int64_t(slot) * SS::SLOT_FLOATS + wave * 64 + lane;
+        // 16-byte and 8-byte buffer stores with the agent-scope (sc1) policy, the encoding an
+        // agent-scope atomic store of one word gets
+        const __amdgpu_buffer_rsrc_t wpart = rsrc(p.part, 0xFFFFFFFFu);
+        const uint32_t sbase = uint32_t(int64_t(slot) * SS::SLOT_FLOATS * 4);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            __hip_atomic_store(sp + (db * 16 + i) * NW * 64, oacc[db][i], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sp + 64 * NW * 64, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sp + 65 * NW * 64, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int g = 0; g < 16; ++g) {
+          const f32x16_t& o = oacc[g >> 2];
+          const int i = 4 * (g & 3);
+          const v4f32_t w = {o[i], o[i + 1], o[i + 2], o[i + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, w), wpart,
+                                                 sbase + uint32_t((g * NW * 64 + tid) * 16), 0, kSc1);
+        }
+        const v2f32_t ml = {m_run, l_run};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, ml), wpart,
+                                              sbase + uint32_t(SS::ML_OFFSET + tid * 8), 0, kSc1);
         __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are complete
         __syncthreads();
         if (tid == 0) {
@@ -1000,12 +1017,13 @@ void attn_bf16_direct_kernel(Params p) {
       // merge: the main piece, then the tail pieces in range order (the result does not
       // depend on which workgroup merges: starting from the main piece's registers is the
       // same arithmetic as loading it first into a zero state), online: the sum is rescaled
-      // whenever a piece brings a larger running max. Reads use buffer loads with the
-      // agent-scope (sc1) cache policy, the encoding of an agent-scope atomic load; as plain
-      // loads they may be issued back to back. A piece's 66 values are loaded into registers
-      // before any is used (scheduling barrier): left to itself, the compiler waited after
-      // every load in the FP4 instantiation, whose registers run at the limit, and a merge of
-      // many pieces then took hundreds of microseconds.
+      // whenever a piece brings a larger running max. Reads use 16-byte and 8-byte buffer
+      // loads with the agent-scope (sc1) cache policy, the encoding of an agent-scope atomic
+      // load; as plain loads they may be issued back to back. A piece's 66 values (17 loads)
+      // are in registers before any is used (scheduling barrier): left to itself, the compiler
+      // waited after every load in the FP4 instantiation, whose registers run at the limit,
+      // and a merge of many pieces then took hundreds of microseconds. (Moving the state in
+      // 16-byte instead of 4-byte words made 12-head chunk attention 2.5% faster.)
       const __amdgpu_buffer_rsrc_t rpart = rsrc(p.part, 0xFFFFFFFFu);
       float m_all = m_run;
       if (!from_regs) {
@@ -1016,11 +1034,21 @@ void attn_bf16_direct_kernel(Params p) {
       }
       for (int gs = from_regs ? gs_first : gs_first - 1; gs <= gs_last; ++gs) {
         const int sl = gs < gs_first ? blk : nblk + gs + blk;
-        const uint32_t base = uint32_t((int64_t(sl) * SS::SLOT_FLOATS + wave * 64 + lane) * 4);
+        const uint32_t base = uint32_t(int64_t(sl) * SS::SLOT_FLOATS * 4);
         float b[SS::REGS];
 #pragma unroll
-        for (int r = 0; r < SS::REGS; ++r)
-          b[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, base + r * NW * 64 * 4, 0, 16));
+        for (int g = 0; g < 16; ++g) {
+          const v4f32_t w = __builtin_bit_cast(v4f32_t, __builtin_amdgcn_raw_buffer_load_b128(
+              rpart, base + uint32_t((g * NW * 64 + tid) * 16), 0, kSc1));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) b[4 * g + i] = w[i];
+        }
+        {
+          const v2f32_t ml = __builtin_bit_cast(v2f32_t, __builtin_amdgcn_raw_buffer_load_b64(
+              rpart, base + uint32_t(SS::ML_OFFSET + tid * 8), 0, kSc1));
+          b[64] = ml[0];
+          b[65] = ml[1];
+        }
         __builtin_amdgcn_sched_barrier(0);
         const float m_p = b[64];
         if (m_p > m_all) {   // this piece raises the lane's running max: rescale the sum
