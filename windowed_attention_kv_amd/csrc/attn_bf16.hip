@@ -566,9 +566,13 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* ld
 // block's counter; the one that sees the count complete merges the slots (main piece
 // first, then the tail pieces in range order) and stores O. No workgroup ever waits on
 // another.
-// A piece's state in its workspace slot: thread t's 64 O values as 16 groups of 4 (group g at
-// byte (g * threads + t) * 16), then its running max and sum as one 8-byte pair (at byte
-// 16 * 16 * threads + 8 t), so both publishing and merging move 16-byte and 8-byte words.
+// A piece's state in its workspace slot. Wide form (the dense chunk-attention instantiation):
+// thread t's 64 O values as 16 groups of 4 (group g at byte (g * threads + t) * 16), then its
+// running max and sum as one 8-byte pair (at byte 16 * 16 * threads + 8 t), so publishing and
+// merging move 16-byte and 8-byte words (12-head chunk attention 2.5% faster than one word per
+// access). Word form (FP4 and fused cross-attention instantiations, where the wide form was
+// 1-2% slower, by code placement: their tile loops are unchanged): value r of thread t at word
+// r * threads + t. A launch runs one instantiation, so its pieces share one form.
 template <int NW>
 struct SplitState {
   static constexpr int REGS = 66;               // 64 O values, running max, running sum
@@ -587,6 +591,7 @@ void attn_bf16_direct_kernel(Params p) {
   constexpr int D = 128;
   using T = DtCfg<SUB>;
   using SS = SplitState<NW>;
+  constexpr bool kWideState = !FP4 && !CROSS;   // piece-state form (SplitState)
   constexpr int DT_TILE = T::TILE, DT_BUF = T::BUF, DT_LDS = T::LDS, TR = T::ROWS;
   constexpr int IPW = DT_TILE / 1024 / NW;  // direct loads per wave per tensor per tile
   static_assert(IPW * NW * 1024 == DT_TILE, "tile must split evenly over the waves");
@@ -986,21 +991,33 @@ void attn_bf16_direct_kernel(Params p) {
         __syncthreads();   // s_last is written again below
       }
       if (!from_regs) {
-        // 16-byte and 8-byte buffer stores with the agent-scope (sc1) policy, the encoding an
-        // agent-scope atomic store of one word gets
-        const __amdgpu_buffer_rsrc_t wpart = rsrc(p.part, 0xFFFFFFFFu);
-        const uint32_t sbase = uint32_t(int64_t(slot) * SS::SLOT_FLOATS * 4);
+        if constexpr (kWideState) {
+          const __amdgpu_buffer_rsrc_t wpart = rsrc(p.part, 0xFFFFFFFFu);
+          const uint32_t sbase = uint32_t(int64_t(slot) * SS::SLOT_FLOATS * 4);
+          // 16-byte and 8-byte buffer stores with the agent-scope (sc1) policy, the encoding
+          // an agent-scope atomic store of one word gets
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          const f32x16_t& o = oacc[g >> 2];
-          const int i = 4 * (g & 3);
-          const v4f32_t w = {o[i], o[i + 1], o[i + 2], o[i + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, w), wpart,
-                                                 sbase + uint32_t((g * NW * 64 + tid) * 16), 0, kSc1);
+          for (int g = 0; g < 16; ++g) {
+            const f32x16_t& o = oacc[g >> 2];
+            const int i = 4 * (g & 3);
+            const v4f32_t w = {o[i], o[i + 1], o[i + 2], o[i + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, w), wpart,
+                                                   sbase + uint32_t((g * NW * 64 + tid) * 16), 0, kSc1);
+          }
+          const v2f32_t ml = {m_run, l_run};
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, ml), wpart,
+                                                sbase + uint32_t(SS::ML_OFFSET + tid * 8), 0, kSc1);
+        } else {
+          float* sp = p.part + int64_t(slot) * SS::SLOT_FLOATS + wave * 64 + lane;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              __hip_atomic_store(sp + (db * 16 + i) * NW * 64, oacc[db][i], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(sp + 64 * NW * 64, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(sp + 65 * NW * 64, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        const v2f32_t ml = {m_run, l_run};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, ml), wpart,
-                                              sbase + uint32_t(SS::ML_OFFSET + tid * 8), 0, kSc1);
         __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are complete
         __syncthreads();
         if (tid == 0) {
@@ -1022,8 +1039,7 @@ void attn_bf16_direct_kernel(Params p) {
       // load; as plain loads they may be issued back to back. A piece's 66 values (17 loads)
       // are in registers before any is used (scheduling barrier): left to itself, the compiler
       // waited after every load in the FP4 instantiation, whose registers run at the limit,
-      // and a merge of many pieces then took hundreds of microseconds. (Moving the state in
-      // 16-byte instead of 4-byte words made 12-head chunk attention 2.5% faster.)
+      // and a merge of many pieces then took hundreds of microseconds.
       const __amdgpu_buffer_rsrc_t rpart = rsrc(p.part, 0xFFFFFFFFu);
       float m_all = m_run;
       if (!from_regs) {
@@ -1034,20 +1050,25 @@ void attn_bf16_direct_kernel(Params p) {
       }
       for (int gs = from_regs ? gs_first : gs_first - 1; gs <= gs_last; ++gs) {
         const int sl = gs < gs_first ? blk : nblk + gs + blk;
-        const uint32_t base = uint32_t(int64_t(sl) * SS::SLOT_FLOATS * 4);
         float b[SS::REGS];
+        if constexpr (kWideState) {
+          const uint32_t base = uint32_t(int64_t(sl) * SS::SLOT_FLOATS * 4);
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          const v4f32_t w = __builtin_bit_cast(v4f32_t, __builtin_amdgcn_raw_buffer_load_b128(
-              rpart, base + uint32_t((g * NW * 64 + tid) * 16), 0, kSc1));
+          for (int g = 0; g < 16; ++g) {
+            const v4f32_t w = __builtin_bit_cast(v4f32_t, __builtin_amdgcn_raw_buffer_load_b128(
+                rpart, base + uint32_t((g * NW * 64 + tid) * 16), 0, kSc1));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) b[4 * g + i] = w[i];
-        }
-        {
+            for (int i = 0; i < 4; ++i) b[4 * g + i] = w[i];
+          }
           const v2f32_t ml = __builtin_bit_cast(v2f32_t, __builtin_amdgcn_raw_buffer_load_b64(
               rpart, base + uint32_t(SS::ML_OFFSET + tid * 8), 0, kSc1));
           b[64] = ml[0];
           b[65] = ml[1];
+        } else {
+          const uint32_t base = uint32_t((int64_t(sl) * SS::SLOT_FLOATS + wave * 64 + lane) * 4);
+#pragma unroll
+          for (int r = 0; r < SS::REGS; ++r)
+            b[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rpart, base + r * NW * 64 * 4, 0, kSc1));
         }
         __builtin_amdgcn_sched_barrier(0);
         const float m_p = b[64];
