@@ -152,6 +152,11 @@ def gen_inputs(torch, n_chunks, n, H, D, seed, device):
 _SLEEP_CYCLES_PER_MS = None
 
 
+def progress(msg):
+    """One progress line on stderr (stdout carries only the JSON result line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def gpu_hold(torch, ms):
     """Enqueue a GPU spin of about `ms` milliseconds (torch's sleep kernel, its cycle count
     calibrated once with events). A start event recorded after it fires only when the spin
@@ -608,6 +613,7 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     inputs = gen_inputs(torch, shape.chunks, n, H, D, 7, "cuda")
     out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
     res["layer_stream"] = layer_stream_row(torch, shape, Cache, attn_flops, inputs)
+    progress("row done: single-layer stream")
     # 30 distinct (K, V) pairs for the commit rows (the 20 chunks' q, k, v tensors, paired up)
     flat = [t for trip in inputs for t in trip]
     pairs = [(flat[2 * i], flat[2 * i + 1]) for i in range(30)]
@@ -619,6 +625,7 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
     res["plain_copy_same_bytes"] = copy_ceiling_row(torch, pairs)
     del pairs, flat
     res["kv_quant_same_bytes_as_fp4_commit"] = quant_chunk_row(torch, inputs[0][1], inputs[0][2])
+    progress("rows done: commits, copy ceiling, codec")
     # FP4 KV store at the layer shape: steady-state attention (15 visible frames)
     c4 = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
                shape.window_frames, kv_format="fp4")
@@ -695,11 +702,15 @@ def extra_rows(torch, shape, Cache, kv_quant, attn_flops):
                                  "frac_hbm": round(qbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del x, pk, sc
     res["recache_30_layers"] = recache_row(torch, shape, Cache, inputs)
+    progress("row done: 30-layer recache")
     pool = gen_inputs(torch, 8, n, H, D, 21, "cuda")
     res["stack_fp4"] = stack_row(torch, shape, Cache, attn_flops, "fp4", pool)
+    progress("row done: FP4 stack")
     res["interactive_composite"] = composite_row(torch, shape, Cache, attn_flops, pool)
+    progress("row done: interactive composite")
     res["gemm_bf16_ceiling"] = gemm_ceiling_row(torch)
     res["vendor_flash_attention_same_shape"] = sdpa_context_row(torch, shape, attn_flops)
+    progress("rows done: vendor context rows")
     return res
 
 
@@ -914,19 +925,23 @@ def main():
     flops_step = stack_flops(shape, attn_flops, L, steps, chunks)
     launches = L * steps * chunks
 
-    for _ in range(args.warmup):
+    for w in range(args.warmup):
         cache.reset()
         stack_pass(cache, pool, out, L, steps, chunks)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        progress(f"warm-up stack pass {w + 1}/{args.warmup} done")
 
     timer = EventTimer(torch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for st in range(args.steps):
         cache.reset()
         stack_pass(cache, pool, out, L, steps, chunks, timer)
+        # enqueued, not synchronised: the host runs at most a launch queue ahead of the GPU
+        progress(f"timed stack pass {st + 1}/{args.steps} enqueued")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    progress(f"timed passes done: {wall * 1e3 / args.steps:.1f} ms per pass")
     tot = timer.totals()
     ms_step = wall * 1e3 / args.steps
     # average attention launch: each chunk's 120 back-to-back attention launches are bracketed
@@ -981,6 +996,7 @@ def main():
     if not args.no_extra:
         line["rows"].update(extra_rows(torch, layer_shape, Cache, kv_quant, attn_flops))
     if not args.no_cpu:
+        progress("CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(layer_shape)
     print(json.dumps(line), flush=True)
 
