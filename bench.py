@@ -76,10 +76,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the FP4 / recache rows")
-    ap.add_argument("--row", choices=["share", "recache", "vendor-flash"], default=None,
+    ap.add_argument("--row", choices=["share", "recache", "vendor-flash", "steady"], default=None,
                     help="run only this workload (for profiling) and print its row: the 3-head "
-                         "share streams, the 30-layer recache or the vendor flash attention "
-                         "on the steady chunk's shape")
+                         "share streams, the 30-layer recache, the vendor flash attention "
+                         "on the steady chunk's shape, or 40 steady 12-head chunk calls")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -745,6 +745,31 @@ def share_rows(torch, shape, Cache, attn_flops, inputs):
     return res
 
 
+def steady_calls_row(torch, shape, Cache, attn_flops, inputs, calls=40):
+    """The steady chunk call alone (12 heads, 4680 query rows over 23,400 keys): a layer is
+    filled with 5 chunks, then the 6th chunk's attention runs `calls` times back to back,
+    events around the batch (behind a GPU spin, gpu_hold), so that a profiler sees those
+    launches only."""
+    n, H, D = shape.n_query, shape.heads, shape.head_dim
+    cache = Cache(1, H, D, shape.tokens_per_frame, shape.chunk_frames, shape.sink_frames,
+                  shape.window_frames)
+    out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+    for q, k, v in inputs[:5]:
+        cache.attn_chunk(0, q, k, v, out=out)
+        cache.commit(0, k, v)
+    q, k, v = inputs[5]
+    tm = EventTimer(torch)
+    s = tm.start(HOLD_MS)
+    for _ in range(calls):
+        cache.attn_chunk(0, q, k, v, out=out)
+    tm.stop(s, "steady")
+    torch.cuda.synchronize()
+    ms = tm.totals()["steady"][0] / calls
+    fl = attn_flops(n, 23400, H, D)
+    return {"calls": calls, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+            "frac_bf16_peak": round(fl / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def recache_row(torch, shape, Cache, inputs):
     """The prompt-switch recache (12 held frames, 512 text tokens) of every layer of a
     filled 30-layer cache: per layer block-causal self + cross + slot rewrite."""
@@ -910,6 +935,8 @@ def main():
             rows = share_rows(torch, ls, Cache, attn_flops, inputs)
         elif args.row == "vendor-flash":
             rows = {"vendor_flash_attention_same_shape": sdpa_context_row(torch, ls, attn_flops)}
+        elif args.row == "steady":
+            rows = {"attention_steady_calls": steady_calls_row(torch, ls, Cache, attn_flops, inputs)}
         else:
             rows = {"recache_30_layers": recache_row(torch, ls, Cache, inputs)}
         print(json.dumps({"row": args.row, "rows": rows}), flush=True)
